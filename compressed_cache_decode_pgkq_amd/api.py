@@ -1,0 +1,189 @@
+"""PyTorch-facing binding of the PGKQ C ABI: argument marshalling only.
+
+Every function has the name of the C entry point it calls.  Tensors must live
+on the GPU; device memory for outputs and workspaces is allocated with PyTorch
+when the caller does not pass it, and work is enqueued on the current PyTorch
+stream.  All arithmetic happens in the HIP kernels of libpgkq.so.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclass(frozen=True)
+class PgkqParams:
+    head_dim: int
+    b_main: int
+    b_angle: int
+    qjl_m: int
+    hadamard: int = 1
+
+    def c(self) -> L.PgkqParams:
+        return L.PgkqParams(self.head_dim, self.b_main, self.b_angle, self.qjl_m, self.hadamard)
+
+
+_DT = {torch.float32: L.PGKQ_F32, torch.float16: L.PGKQ_F16, torch.bfloat16: L.PGKQ_BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("PGKQ entry points take device tensors")
+    if not t.is_contiguous():
+        raise ValueError("PGKQ entry points take contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _opts(n_splits: int, events):
+    o = L.PgkqLaunchOpts(int(n_splits), None, None)
+    if events is not None:
+        o.scan_start = ctypes.c_void_p(events[0].cuda_event)
+        o.scan_stop = ctypes.c_void_p(events[1].cuda_event)
+    return o
+
+
+def _ws(nbytes: int, device, workspace):
+    if nbytes == 0:
+        return workspace, 0
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def pgkq_version() -> str:
+    return L.lib().pgkq_version().decode()
+
+
+def pgkq_record_bytes(params: PgkqParams) -> int:
+    return int(L.lib().pgkq_record_bytes(ctypes.byref(params.c())))
+
+
+def pgkq_codes_bytes(params: PgkqParams, n_streams: int, capacity: int) -> int:
+    return int(L.lib().pgkq_codes_bytes(ctypes.byref(params.c()), n_streams, capacity))
+
+
+def pgkq_lloyd_max_beta(head_dim: int, b_main: int):
+    n = 1 << b_main
+    lv = (ctypes.c_double * n)()
+    th = (ctypes.c_double * max(n - 1, 1))()
+    L.check(L.lib().pgkq_lloyd_max_beta(head_dim, b_main, lv, th), "pgkq_lloyd_max_beta")
+    return np.array(lv[:], dtype=np.float64), np.array(th[: n - 1], dtype=np.float64)
+
+
+def pgkq_calibrate(params: PgkqParams, K: torch.Tensor, reorder: bool = False, stream=None):
+    """K [n_seq, n_kv, n_tokens, d] -> (sumsq [n_kv, d] f64, perm [n_kv, d] i16 bits of u16,
+    codebook [n_kv, 2L] f32)."""
+    n_seq, n_kv, n_tok, d = K.shape
+    p = params.c()
+    dev = K.device
+    sumsq = torch.empty((n_kv, d), dtype=torch.float64, device=dev)
+    perm = torch.empty((n_kv, d), dtype=torch.int16, device=dev)
+    cb = torch.empty((n_kv, 2 << params.b_main), dtype=torch.float32, device=dev)
+    nb = int(L.lib().pgkq_calibrate_workspace_bytes(ctypes.byref(p), n_seq, n_kv, n_tok))
+    ws, wsb = _ws(max(nb, 256), dev, None)
+    st = L.lib().pgkq_calibrate(ctypes.byref(p), _ptr(K), _dtype(K), n_seq, n_kv, n_tok,
+                                1 if reorder else 0, _ptr(sumsq), _ptr(perm), _ptr(cb), _ptr(ws),
+                                wsb, _stream(stream))
+    L.check(st, "pgkq_calibrate")
+    return sumsq, perm, cb
+
+
+def pgkq_encode(params: PgkqParams, K: torch.Tensor, signs: torch.Tensor, perm, codebook,
+                S, codes=None, capacity=None, token_offset: int = 0, stream=None):
+    """Encode K [n_seq, n_kv, n_tokens, d] into codes [n_seq, n_kv, capacity * record] uint8."""
+    n_seq, n_kv, n_tok, d = K.shape
+    cap = int(capacity) if capacity is not None else n_tok
+    p = params.c()
+    if codes is None:
+        rb = pgkq_record_bytes(params)
+        codes = torch.zeros((n_seq, n_kv, cap * rb), dtype=torch.uint8, device=K.device)
+    st = L.lib().pgkq_encode(ctypes.byref(p), _ptr(K), _dtype(K), n_seq, n_kv, n_tok, _ptr(signs),
+                             _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes), cap,
+                             int(token_offset), _stream(stream))
+    L.check(st, "pgkq_encode")
+    return codes
+
+
+def pgkq_decode_workspace_bytes(params: PgkqParams, n_seq, n_q, n_kv, n_tokens, n_splits=0) -> int:
+    o = _opts(n_splits, None)
+    return int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(params.c()), n_seq, n_q, n_kv,
+                                                    n_tokens, ctypes.byref(o)))
+
+
+def pgkq_decode_attn(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, V: torch.Tensor,
+                     signs, perm, codebook, S, n_tokens=None, softmax_scale: float = 0.0,
+                     n_splits: int = 0, out=None, workspace=None, events=None, stream=None):
+    """q [n_seq, n_q, d]; codes [n_seq, n_kv, cap * record]; V [n_seq, n_kv, cap, d] fp16."""
+    n_seq, n_q, d = q.shape
+    n_kv, cap = V.shape[1], V.shape[2]
+    n_tok = cap if n_tokens is None else int(n_tokens)
+    p = params.c()
+    o = _opts(n_splits, events)
+    if out is None:
+        out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    nb = int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(p), n_seq, n_q, n_kv, n_tok,
+                                                  ctypes.byref(o)))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_decode_attn(ctypes.byref(p), _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap,
+                                  _ptr(signs), _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes),
+                                  _ptr(V), _ptr(out), float(softmax_scale), ctypes.byref(o),
+                                  _ptr(ws), wsb, _stream(stream))
+    L.check(st, "pgkq_decode_attn")
+    return out
+
+
+def pgkq_estimate_logits(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, n_kv: int,
+                         capacity: int, signs, perm, codebook, S, n_tokens=None, logits=None,
+                         workspace=None, stream=None):
+    """Raw logits [n_seq, n_q, n_tokens] fp32 (no softmax scale)."""
+    n_seq, n_q, d = q.shape
+    n_tok = capacity if n_tokens is None else int(n_tokens)
+    p = params.c()
+    if logits is None:
+        logits = torch.empty((n_seq, n_q, n_tok), dtype=torch.float32, device=q.device)
+    nb = int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(p), n_seq, n_q, n_kv, n_tok, None))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_estimate_logits(ctypes.byref(p), _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok,
+                                      capacity, _ptr(signs), _ptr(perm), _ptr(codebook), _ptr(S),
+                                      _ptr(codes), _ptr(logits), _ptr(ws), wsb, _stream(stream))
+    L.check(st, "pgkq_estimate_logits")
+    return logits
+
+
+def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor, n_tokens=None,
+                          softmax_scale: float = 0.0, n_splits: int = 0, out=None, workspace=None,
+                          events=None, stream=None):
+    n_seq, n_q, d = q.shape
+    n_kv, cap = K16.shape[1], K16.shape[2]
+    n_tok = cap if n_tokens is None else int(n_tokens)
+    o = _opts(n_splits, events)
+    if out is None:
+        out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    nb = int(L.lib().pgkq_fp16_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, ctypes.byref(o)))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_fp16_decode_attn(_ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap, d,
+                                       _ptr(K16), _ptr(V16), _ptr(out), float(softmax_scale),
+                                       ctypes.byref(o), _ptr(ws) if ws is not None else None, wsb,
+                                       _stream(stream))
+    L.check(st, "pgkq_fp16_decode_attn")
+    return out

@@ -1,0 +1,117 @@
+// Device helpers shared by the PGKQ kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pgkq_internal.hpp"
+
+namespace pgkq {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float load_f(const void* p, int dtype, int64_t i) {
+  if (dtype == DT_F32) return static_cast<const float*>(p)[i];
+  if (dtype == DT_F16) return __half2float(static_cast<const __half*>(p)[i]);
+  // bf16: the upper half of an fp32
+  uint32_t u = static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+
+// fp64 -> fp16 bits, round to nearest (ties to even), values beyond the fp16
+// range saturate to 65504.  Written on the bit pattern so that exactly one
+// rounding happens (no detour through fp32).  Only non-negative inputs occur
+// (residual norms); the sign is carried anyway.
+__device__ __forceinline__ uint16_t f64_to_f16_rne_sat(double x) {
+  uint64_t b = static_cast<uint64_t>(__double_as_longlong(x));
+  uint16_t sign = static_cast<uint16_t>((b >> 48) & 0x8000u);
+  uint64_t mag = b & 0x7FFFFFFFFFFFFFFFull;
+  if (mag >= 0x7FF0000000000000ull) {  // inf or nan
+    return mag == 0x7FF0000000000000ull ? static_cast<uint16_t>(sign | 0x7BFFu)
+                                        : static_cast<uint16_t>(sign | 0x7E00u);
+  }
+  int e = static_cast<int>(mag >> 52);  // biased fp64 exponent
+  uint64_t m = mag & 0x000FFFFFFFFFFFFFull;
+  int eh = e - 1023 + 15;               // biased fp16 exponent
+  if (eh >= 31) return static_cast<uint16_t>(sign | 0x7BFFu);
+  uint64_t full;   // significand with the implicit bit
+  int shift;       // bits to drop from the 53-bit significand
+  if (e == 0) return sign;  // fp64 subnormal: far below the fp16 range
+  full = m | 0x0010000000000000ull;
+  if (eh >= 1) {
+    shift = 42;  // keep 11 significant bits
+  } else {
+    shift = 42 + (1 - eh);  // fp16 subnormal
+    if (shift > 63) return sign;
+  }
+  uint64_t kept = full >> shift;
+  uint64_t rem = full & ((1ull << shift) - 1);
+  uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (kept & 1))) kept += 1;
+  uint32_t out;
+  if (eh >= 1) {
+    // kept in [2^10, 2^11]; a carry to 2^11 bumps the exponent
+    uint32_t ee = static_cast<uint32_t>(eh);
+    if (kept == (1ull << 11)) { kept = 1ull << 10; ee += 1; }
+    if (ee >= 31) return static_cast<uint16_t>(sign | 0x7BFFu);
+    out = (ee << 10) | static_cast<uint32_t>(kept & 0x3FFu);
+  } else {
+    // subnormal result; a carry into 2^10 yields the smallest normal naturally
+    out = static_cast<uint32_t>(kept);
+  }
+  return static_cast<uint16_t>(sign | out);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// double exchanged with the lane whose index differs in bit `mask` (1 or 2):
+// DPP quad permutation, no LDS traffic.
+template <int MASK>
+__device__ __forceinline__ double quad_xor(double v) {
+  static_assert(MASK == 1 || MASK == 2, "quad permutation only");
+  constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  int lo = __double2loint(v), hi = __double2hiint(v);
+  lo = __builtin_amdgcn_mov_dpp(lo, ctrl, 0xF, 0xF, true);
+  hi = __builtin_amdgcn_mov_dpp(hi, ctrl, 0xF, 0xF, true);
+  return __hiloint2double(hi, lo);
+}
+
+template <int MASK>
+__device__ __forceinline__ float quad_xor_f(float v) {
+  static_assert(MASK == 1 || MASK == 2, "quad permutation only");
+  constexpr int ctrl = (MASK == 1) ? 0xB1 : 0x4E;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true));
+}
+
+// Cell of the mid-rise angle grid with 8 cells of width pi/4 starting at -pi,
+// decided by exact comparisons: the cell holding direction (x, y) when cells
+// are half-open [e_a, e_{a+1}) counter-clockwise, theta = pi counted as -pi
+// (cell 0), and the zero vector taken as theta = 0 (cell 4).  Coarser grids
+// are prefixes: cell_b = cell_3 >> (3 - b).
+__device__ __forceinline__ int octant_cell(double x, double y) {
+  if (x == 0.0 && y == 0.0) return 4;
+  const bool hi = (y > 0.0) || (y == 0.0 && x > 0.0);
+  const bool quarter = hi ? (x <= 0.0) : (x >= 0.0);
+  const double ax = fabs(x), ay = fabs(y);
+  const bool sub = quarter ? (ay <= ax) : (ay >= ax);
+  return (hi ? 4 : 0) + (quarter ? 2 : 0) + (sub ? 1 : 0);
+}
+
+}  // namespace pgkq

@@ -1,0 +1,507 @@
+// C-ABI host layer of the PGKQ library: argument validation, workspace
+// sizing, split selection and kernel dispatch, plus the host-side Lloyd-Max
+// codebook for the Beta radius prior.  See include/pgkq.h for the contract.
+#include "pgkq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "pgkq_internal.hpp"
+
+namespace {
+
+using pgkq::Geometry;
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+pgkq_status check_params(const pgkq_params* p, Geometry* g) {
+  if (!p) return PGKQ_ERR_NULL;
+  if (p->head_dim != 64 && p->head_dim != 128) return PGKQ_ERR_UNSUPPORTED;
+  if (p->b_main < 2 || p->b_main > 4) return PGKQ_ERR_UNSUPPORTED;
+  if (p->b_angle != p->b_main - 1) return PGKQ_ERR_UNSUPPORTED;
+  if (p->qjl_m != 0 && p->qjl_m != p->head_dim) return PGKQ_ERR_UNSUPPORTED;
+  if (p->hadamard != 0 && p->hadamard != 1) return PGKQ_ERR_UNSUPPORTED;
+  if (g) *g = Geometry{p->head_dim, p->b_main, p->b_angle, p->qjl_m, p->hadamard};
+  return PGKQ_OK;
+}
+
+pgkq_status check_dtype(pgkq_dtype t, bool allow_bf16) {
+  if (t == PGKQ_F32 || t == PGKQ_F16) return PGKQ_OK;
+  if (t == PGKQ_BF16 && allow_bf16) return PGKQ_OK;
+  return PGKQ_ERR_UNSUPPORTED;
+}
+
+pgkq_status check_streams(int64_t n_seq, int64_t n_kv) {
+  if (n_seq < 1 || n_kv < 1) return PGKQ_ERR_SHAPE;
+  if (n_seq > kMaxGridYZ || n_kv > kMaxGridYZ) return PGKQ_ERR_SHAPE;
+  return PGKQ_OK;
+}
+
+pgkq_status check_group(int64_t n_q, int64_t n_kv, int* group) {
+  if (n_q < 1 || n_q % n_kv != 0) return PGKQ_ERR_SHAPE;
+  const int64_t g = n_q / n_kv;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return PGKQ_ERR_UNSUPPORTED;
+  if (n_q > kMaxGridYZ) return PGKQ_ERR_SHAPE;
+  *group = static_cast<int>(g);
+  return PGKQ_OK;
+}
+
+pgkq_status map_hip(hipError_t e) { return e == hipSuccess ? PGKQ_OK : PGKQ_ERR_HIP; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Splits {
+  int n;
+  int64_t tokens_per;
+};
+
+// Token splits per (sequence, kv-head): enough workgroups to cover the chip
+// (about 2048 in flight) without splits shorter than one wavefront chunk.
+Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested) {
+  int64_t ns = requested > 0 ? requested : (2048 + n_units - 1) / n_units;
+  const int64_t min_tokens = requested > 0 ? 64 : 256;
+  const int64_t max_ns = std::max<int64_t>(1, (n_tokens + min_tokens - 1) / min_tokens);
+  ns = std::min<int64_t>(std::max<int64_t>(ns, 1), max_ns);
+  int64_t tps = (n_tokens + ns - 1) / ns;
+  tps = std::max<int64_t>(64, round_up(static_cast<size_t>(tps), 64));
+  ns = std::max<int64_t>(1, (n_tokens + tps - 1) / tps);
+  return Splits{static_cast<int>(ns), tps};
+}
+
+size_t decode_ws(const Geometry& g, int64_t n_seq, int64_t n_q, const Splits& sp) {
+  const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
+  size_t bytes = round_up(size_t(n_seq) * n_q * pl.stride() * sizeof(float), 256);
+  if (sp.n > 1) bytes += round_up(size_t(n_seq) * n_q * sp.n * (g.d + 4) * sizeof(float), 256);
+  return bytes;
+}
+
+size_t fp16_ws(int d, int64_t n_seq, int64_t n_q, const Splits& sp) {
+  if (sp.n <= 1) return 0;
+  return round_up(size_t(n_seq) * n_q * sp.n * (d + 4) * sizeof(float), 256);
+}
+
+__global__ void zero_fill_kernel(float* p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += size_t(gridDim.x) * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096));
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Lloyd-Max
+
+// Gauss-Legendre nodes and weights on [-1, 1] (Newton iteration on P_N).
+void gauss_legendre(int N, std::vector<double>& x, std::vector<double>& w) {
+  x.assign(N, 0.0);
+  w.assign(N, 0.0);
+  const double pi = 3.14159265358979323846;
+  for (int i = 0; i < N; ++i) {
+    double z = std::cos(pi * (i + 0.75) / (N + 0.5));
+    double dp = 1.0;
+    for (int it = 0; it < 100; ++it) {
+      double p0 = 1.0, p1 = 0.0;
+      for (int j = 1; j <= N; ++j) {
+        const double p2 = p1;
+        p1 = p0;
+        p0 = ((2.0 * j - 1.0) * z * p1 - (j - 1.0) * p2) / j;
+      }
+      dp = N * (z * p0 - p1) / (z * z - 1.0);
+      const double dz = p0 / dp;
+      z -= dz;
+      if (std::fabs(dz) < 1e-16) break;
+    }
+    x[i] = z;
+    w[i] = 2.0 / ((1.0 - z * z) * dp * dp);
+  }
+}
+
+// rho = (r/||k||) sqrt(n), n = d/2 pairs: F(rho) = 1 - (1 - rho^2/n)^(n-1);
+// rho f(rho) = (2 (n-1)/n) rho^2 (1 - rho^2/n)^(n-2) is a polynomial of degree
+// 2n - 2, so an (n + 4)-point Gauss-Legendre rule integrates it exactly.
+struct BetaPrior {
+  int n;
+  std::vector<double> gx, gw;
+  explicit BetaPrior(int n_) : n(n_) { gauss_legendre(n + 4, gx, gw); }
+  double cdf(double rho) const {
+    double u = rho * rho / n;
+    if (u >= 1.0) return 1.0;
+    return -std::expm1((n - 1) * std::log1p(-u));
+  }
+  double quantile(double p) const {
+    const double u = -std::expm1(std::log1p(-p) / (n - 1));
+    return std::sqrt(n * u);
+  }
+  double moment(double a, double b) const {
+    const double half = 0.5 * (b - a), mid = 0.5 * (a + b);
+    double s = 0.0;
+    for (size_t i = 0; i < gx.size(); ++i) {
+      const double r = mid + half * gx[i];
+      const double u = 1.0 - r * r / n;
+      s += gw[i] * r * r * std::pow(u, n - 2);
+    }
+    return half * s * (2.0 * (n - 1) / n);
+  }
+};
+
+pgkq_status lloyd_max(int head_dim, int b_main, double* levels, double* thresholds) {
+  const int n = head_dim / 2;
+  const int L = 1 << b_main;
+  BetaPrior pr(n);
+  const double top = std::sqrt(double(n));
+  std::vector<double> c(L), e(L + 1), cn(L);
+  for (int j = 0; j < L; ++j) c[j] = pr.quantile((j + 0.5) / L);
+  bool done = false;
+  for (int it = 0; it < 200000 && !done; ++it) {
+    e[0] = 0.0;
+    e[L] = top;
+    for (int j = 1; j < L; ++j) e[j] = 0.5 * (c[j - 1] + c[j]);
+    double moved = 0.0;
+    for (int j = 0; j < L; ++j) {
+      const double P = pr.cdf(e[j + 1]) - pr.cdf(e[j]);
+      cn[j] = pr.moment(e[j], e[j + 1]) / P;
+      moved = std::max(moved, std::fabs(cn[j] - c[j]));
+    }
+    c = cn;
+    done = moved < 1e-13;
+  }
+  if (!done) return PGKQ_ERR_UNSUPPORTED;
+  for (int j = 0; j < L; ++j) levels[j] = c[j];
+  for (int j = 0; j + 1 < L; ++j) thresholds[j] = 0.5 * (c[j] + c[j + 1]);
+  return PGKQ_OK;
+}
+
+struct TableCache {
+  std::mutex mu;
+  bool have[2][5] = {};
+  double lv[2][5][16];
+  double th[2][5][16];
+};
+TableCache g_tables;
+
+pgkq_status unit_table(int d, int bm, double* lv, double* th) {
+  const int di = d == 64 ? 0 : 1;
+  std::lock_guard<std::mutex> lock(g_tables.mu);
+  if (!g_tables.have[di][bm]) {
+    pgkq_status st = lloyd_max(d, bm, g_tables.lv[di][bm], g_tables.th[di][bm]);
+    if (st != PGKQ_OK) return st;
+    g_tables.have[di][bm] = true;
+  }
+  std::memcpy(lv, g_tables.lv[di][bm], sizeof(double) * 16);
+  std::memcpy(th, g_tables.th[di][bm], sizeof(double) * 16);
+  return PGKQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pgkq_status_string(pgkq_status s) {
+  switch (s) {
+    case PGKQ_OK: return "ok";
+    case PGKQ_ERR_NULL: return "null pointer";
+    case PGKQ_ERR_SHAPE: return "invalid shape";
+    case PGKQ_ERR_UNSUPPORTED: return "unsupported parameters";
+    case PGKQ_ERR_ALIGN: return "misaligned pointer";
+    case PGKQ_ERR_WORKSPACE: return "workspace too small";
+    case PGKQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* pgkq_version(void) { return "pgkq-mi355x 0.1 (gfx950)"; }
+
+size_t pgkq_record_bytes(const pgkq_params* p) {
+  Geometry g;
+  if (check_params(p, &g) != PGKQ_OK) return 0;
+  return g.record_bytes();
+}
+
+size_t pgkq_codes_bytes(const pgkq_params* p, int64_t n_streams, int64_t capacity) {
+  const size_t rb = pgkq_record_bytes(p);
+  if (rb == 0 || n_streams < 0 || capacity < 0) return 0;
+  return rb * size_t(n_streams) * size_t(capacity);
+}
+
+pgkq_status pgkq_lloyd_max_beta(int32_t head_dim, int32_t b_main, double* levels_host,
+                                double* thresholds_host) {
+  if (!levels_host || !thresholds_host) return PGKQ_ERR_NULL;
+  if (head_dim < 4 || head_dim > 4096 || (head_dim & 1)) return PGKQ_ERR_UNSUPPORTED;
+  if (b_main < 1 || b_main > 8) return PGKQ_ERR_UNSUPPORTED;
+  try {
+    return lloyd_max(head_dim, b_main, levels_host, thresholds_host);
+  } catch (...) {
+    return PGKQ_ERR_HIP;
+  }
+}
+
+size_t pgkq_calibrate_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_kv,
+                                      int64_t n_tokens) {
+  Geometry g;
+  if (check_params(p, &g) != PGKQ_OK || n_seq < 1 || n_kv < 1 || n_tokens < 1) return 0;
+  const int64_t rows = n_seq * n_tokens;
+  const int64_t chunks = (rows + 4095) / 4096;
+  return round_up(size_t(n_kv) * chunks * g.d * sizeof(double), 256);
+}
+
+pgkq_status pgkq_calibrate(const pgkq_params* p, const void* K, pgkq_dtype k_dtype, int64_t n_seq,
+                           int64_t n_kv, int64_t n_tokens, int32_t reorder, double* sumsq,
+                           uint16_t* perm, float* codebook, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  Geometry g;
+  pgkq_status st = check_params(p, &g);
+  if (st != PGKQ_OK) return st;
+  if (!K || !sumsq || !codebook || !workspace) return PGKQ_ERR_NULL;
+  if (reorder && !perm) return PGKQ_ERR_NULL;
+  if ((st = check_dtype(k_dtype, false)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  if (n_tokens < 1) return PGKQ_ERR_SHAPE;
+  if (!aligned16(K) || !aligned16(sumsq) || !aligned16(codebook) || !aligned16(workspace) ||
+      (perm && !aligned16(perm)))
+    return PGKQ_ERR_ALIGN;
+  const size_t need = pgkq_calibrate_workspace_bytes(p, n_seq, n_kv, n_tokens);
+  if (workspace_bytes < need) return PGKQ_ERR_WORKSPACE;
+  pgkq::CalibArgs a{};
+  a.K = K;
+  a.k_dtype = static_cast<int>(k_dtype);
+  a.d = g.d;
+  a.n_seq = n_seq;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.rows_per_chunk = 4096;
+  a.n_chunks = (n_seq * n_tokens + 4095) / 4096;
+  if (a.n_chunks > 0x7FFFFFFF) return PGKQ_ERR_SHAPE;
+  a.partial = static_cast<double*>(workspace);
+  a.sumsq = sumsq;
+  a.perm = perm;
+  a.codebook = codebook;
+  a.reorder = reorder ? 1 : 0;
+  a.L = 1 << g.bm;
+  st = unit_table(g.d, g.bm, a.base_levels, a.base_thresholds);
+  if (st != PGKQ_OK) return st;
+  return map_hip(pgkq::launch_calibrate(a, static_cast<hipStream_t>(stream)));
+}
+
+pgkq_status pgkq_encode(const pgkq_params* p, const void* K, pgkq_dtype k_dtype, int64_t n_seq,
+                        int64_t n_kv, int64_t n_tokens, const int8_t* signs, const uint16_t* perm,
+                        const float* codebook, const float* S, void* codes, int64_t capacity,
+                        int64_t token_offset, void* stream) {
+  Geometry g;
+  pgkq_status st = check_params(p, &g);
+  if (st != PGKQ_OK) return st;
+  if (!K || !signs || !codebook || !codes) return PGKQ_ERR_NULL;
+  if (g.m && !S) return PGKQ_ERR_NULL;
+  if ((st = check_dtype(k_dtype, false)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  if (n_tokens < 0 || token_offset < 0 || capacity < 1) return PGKQ_ERR_SHAPE;
+  if (token_offset + n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;  // keeps every stream 4-byte aligned
+  if ((n_tokens + 63) / 64 > 0x7FFFFFFF) return PGKQ_ERR_SHAPE;
+  if (!aligned16(K) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
+      (perm && !aligned16(perm)) || (S && !aligned16(S)))
+    return PGKQ_ERR_ALIGN;
+  if (n_tokens == 0) return PGKQ_OK;
+  pgkq::EncodeArgs a{};
+  a.K = K;
+  a.k_dtype = static_cast<int>(k_dtype);
+  a.hadamard = g.hadamard;
+  a.n_seq = n_seq;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.token_offset = token_offset;
+  a.signs = signs;
+  a.perm = perm;
+  a.codebook = codebook;
+  a.S = g.m ? S : nullptr;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.stream_bytes = size_t(capacity) * g.record_bytes();
+  return map_hip(pgkq::launch_encode(g, a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_q, int64_t n_kv,
+                                   int64_t n_tokens, const pgkq_launch_opts* opts) {
+  Geometry g;
+  if (check_params(p, &g) != PGKQ_OK || n_seq < 1 || n_q < 1 || n_kv < 1 || n_tokens < 0) return 0;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  return decode_ws(g, n_seq, n_q, sp);
+}
+
+static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                                 int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                 int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                                 const float* codebook, const float* S, const void* codes,
+                                 const void* V, float* out, float* logits, float softmax_scale,
+                                 const pgkq_launch_opts* opts, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  Geometry g;
+  pgkq_status st = check_params(p, &g);
+  if (st != PGKQ_OK) return st;
+  const bool logits_mode = logits != nullptr;
+  if (!q || !signs || !codebook || !codes || !workspace) return PGKQ_ERR_NULL;
+  if (!logits_mode && (!V || !out)) return PGKQ_ERR_NULL;
+  if (g.m && !S) return PGKQ_ERR_NULL;
+  if ((st = check_dtype(q_dtype, true)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  int group = 0;
+  if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
+  if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
+      !aligned16(workspace) || (perm && !aligned16(perm)) || (S && !aligned16(S)) ||
+      (V && !aligned16(V)) || (out && !aligned16(out)) || (logits && !aligned16(logits)))
+    return PGKQ_ERR_ALIGN;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  if (workspace_bytes < decode_ws(g, n_seq, n_q, sp)) return PGKQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tokens == 0) {
+    if (logits_mode) return PGKQ_OK;
+    return map_hip(zero_fill(out, size_t(n_seq) * n_q * g.d, s));
+  }
+  const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
+  pgkq::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = static_cast<int>(q_dtype);
+  a.hadamard = g.hadamard;
+  a.n_seq = n_seq;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.group = group;
+  a.signs = signs;
+  a.perm = perm;
+  a.codebook = codebook;
+  a.S = g.m ? S : nullptr;
+  a.codes = static_cast<const uint8_t*>(codes);
+  a.stream_bytes = size_t(capacity) * g.record_bytes();
+  a.V = static_cast<const __half*>(V);
+  a.out = out;
+  a.logits = logits;
+  a.prep = static_cast<float*>(workspace);
+  a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       round_up(size_t(n_seq) * n_q * pl.stride() * 4, 256));
+  a.n_splits = logits_mode ? sp.n : sp.n;
+  a.tokens_per_split = sp.tokens_per;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(g.d));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pgkq::launch_query_prep(g, a, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_start) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  e = pgkq::launch_decode_scan(g, a, logits_mode, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_stop) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  if (!logits_mode && a.n_splits > 1) {
+    e = pgkq::launch_partial_merge(g.d, n_seq, n_q, a.n_splits, a.partial, out, s);
+    if (e != hipSuccess) return PGKQ_ERR_HIP;
+  }
+  return PGKQ_OK;
+}
+
+pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_dtype, int64_t n_seq,
+                             int64_t n_q, int64_t n_kv, int64_t n_tokens, int64_t capacity,
+                             const int8_t* signs, const uint16_t* perm, const float* codebook,
+                             const float* S, const void* codes, const void* V, float* out,
+                             float softmax_scale, const pgkq_launch_opts* opts, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!out) return PGKQ_ERR_NULL;
+  return decode_common(p, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, signs, perm, codebook,
+                       S, codes, V, out, nullptr, softmax_scale, opts, workspace, workspace_bytes,
+                       stream);
+}
+
+pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                                 int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                 int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                                 const float* codebook, const float* S, const void* codes,
+                                 float* logits, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (!logits) return PGKQ_ERR_NULL;
+  return decode_common(p, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, signs, perm, codebook,
+                       S, codes, nullptr, nullptr, logits, 0.f, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q,
+                                        int64_t n_kv, int64_t n_tokens,
+                                        const pgkq_launch_opts* opts) {
+  if ((head_dim != 64 && head_dim != 128) || n_seq < 1 || n_q < 1 || n_kv < 1 || n_tokens < 0)
+    return 0;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  return fp16_ws(head_dim, n_seq, n_q, sp);
+}
+
+pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q,
+                                  int64_t n_kv, int64_t n_tokens, int64_t capacity,
+                                  int32_t head_dim, const void* K16, const void* V16, float* out,
+                                  float softmax_scale, const pgkq_launch_opts* opts,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (head_dim != 64 && head_dim != 128) return PGKQ_ERR_UNSUPPORTED;
+  if (!q || !K16 || !V16 || !out) return PGKQ_ERR_NULL;
+  pgkq_status st;
+  if ((st = check_dtype(q_dtype, true)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  int group = 0;
+  if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
+  if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(K16) || !aligned16(V16) || !aligned16(out) ||
+      (workspace && !aligned16(workspace)))
+    return PGKQ_ERR_ALIGN;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  const size_t need = fp16_ws(head_dim, n_seq, n_q, sp);
+  if (need && (!workspace || workspace_bytes < need)) return PGKQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tokens == 0) return map_hip(zero_fill(out, size_t(n_seq) * n_q * head_dim, s));
+  pgkq::Fp16DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = static_cast<int>(q_dtype);
+  a.d = head_dim;
+  a.n_seq = n_seq;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.group = group;
+  a.K = static_cast<const __half*>(K16);
+  a.V = static_cast<const __half*>(V16);
+  a.out = out;
+  a.partial = static_cast<float*>(workspace);
+  a.n_splits = sp.n;
+  a.tokens_per_split = sp.tokens_per;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (opts && opts->scan_start) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  hipError_t e = pgkq::launch_fp16_decode(a, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_stop) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  if (sp.n > 1) return map_hip(pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.n, a.partial, out, s));
+  return PGKQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Internal interface between the C-ABI host layer (pgkq_host.cpp) and the
+// kernel translation units.  Not installed; the public interface is pgkq.h.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pgkq {
+
+enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+
+struct Geometry {
+  int d;        // head_dim
+  int bm;       // radius bits
+  int ba;       // angle bits
+  int m;        // QJL sketch size (0 = off)
+  int hadamard; // 1 = randomized Hadamard, 0 = identity
+  int P() const { return bm + ba; }
+  int n() const { return d / 2; }
+  int code_words() const { return n() * P() / 32; }
+  int words() const { return code_words() + m / 32; }
+  size_t record_bytes() const { return size_t(4) * words() + (m ? 2 : 0); }
+};
+
+struct EncodeArgs {
+  const void* K;
+  int k_dtype;
+  int hadamard;
+  int64_t n_seq, n_kv, n_tokens, capacity, token_offset;
+  const int8_t* signs;
+  const uint16_t* perm;  // may be null
+  const float* codebook; // [n_kv][2L]
+  const float* S;        // [n_kv][m][d] or null
+  uint8_t* codes;
+  size_t stream_bytes;   // capacity * record_bytes
+};
+
+struct CalibArgs {
+  const void* K;
+  int k_dtype;
+  int d;
+  int64_t n_seq, n_kv, n_tokens;
+  int64_t rows_per_chunk;
+  int64_t n_chunks;
+  double* partial;  // [n_kv][n_chunks][d]
+  double* sumsq;    // [n_kv][d]
+  uint16_t* perm;   // [n_kv][d] or null
+  float* codebook;  // [n_kv][2L]
+  int reorder;
+  int L;
+  double base_levels[16];
+  double base_thresholds[16];
+};
+
+// Query preparation output per (sequence, query head), floats:
+//   [ q~ (d) | angle LUT (n * A) | S q~ (m) | pad to a multiple of 4 ]
+struct PrepLayout {
+  int d, n, A, m;
+  __host__ __device__ int off_lut() const { return d; }
+  __host__ __device__ int off_sq() const { return d + n * A; }
+  __host__ __device__ int stride() const { return ((d + n * A + m) + 3) & ~3; }
+};
+
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  int hadamard;
+  int64_t n_seq, n_q, n_kv, n_tokens, capacity;
+  int group;            // n_q / n_kv
+  const int8_t* signs;
+  const uint16_t* perm;
+  const float* codebook;
+  const float* S;
+  const uint8_t* codes;
+  size_t stream_bytes;
+  const __half* V;
+  float* out;           // final output (n_splits == 1) or null
+  float* logits;        // logits mode output or null
+  float* prep;          // workspace: query prep
+  float* partial;       // workspace: split partial states [n_seq][n_q][n_splits][d + 4]
+  int n_splits;
+  int64_t tokens_per_split;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+struct Fp16DecodeArgs {
+  const void* q;
+  int q_dtype;
+  int d;
+  int64_t n_seq, n_q, n_kv, n_tokens, capacity;
+  int group;
+  const __half* K;
+  const __half* V;
+  float* out;
+  float* partial;
+  int n_splits;
+  int64_t tokens_per_split;
+  float scale_log2;
+};
+
+hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
+hipError_t launch_encode(const Geometry& g, const EncodeArgs& a, hipStream_t s);
+hipError_t launch_query_prep(const Geometry& g, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_scan(const Geometry& g, const DecodeArgs& a, bool logits_mode,
+                              hipStream_t s);
+hipError_t launch_partial_merge(int d, int64_t n_seq, int64_t n_q, int n_splits,
+                                const float* partial, float* out, hipStream_t s);
+hipError_t launch_fp16_decode(const Fp16DecodeArgs& a, hipStream_t s);
+
+}  // namespace pgkq

@@ -1,0 +1,195 @@
+/*
+ * pgkq.h - C ABI of the PGKQ compressed-key cache library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * PGKQ (polar-guided key-cache quantization) is described on the EdgeLLM-Nano
+ * paper page (signal-papers read view of arXiv 2610.14475), paragraph "PGKQ
+ * pipeline" and the codebook paragraph after it, with the record size fixed by
+ * the "Bit budget" paragraph.  Per key vector k of one (layer, kv-head):
+ *   (0) optional channel reorder by decreasing l2 norm, high/low interleaved;
+ *   (1) randomized Hadamard transform k~ = H (signs * k[perm]) / sqrt(d);
+ *   (2) adjacent pairs (k~[2i], k~[2i+1]) -> polar radius r_i and angle theta_i;
+ *   (3) r_i -> b_main-bit Lloyd-Max code (Beta prior), theta_i -> b_angle-bit
+ *       code on a uniform mid-rise grid over [-pi, pi], b_angle = b_main - 1;
+ *   (4) optional QJL residual: signs of S_h (k~ - k~hat) (m = head_dim bits)
+ *       plus one fp16 residual norm.
+ * Decode never rebuilds the keys: logits come from per-query lookup tables over
+ * the codes plus the QJL correction, then softmax and the FP16-V weighted sum.
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers unless the argument says "host".
+ *    The caller owns all memory; the library allocates nothing and keeps no
+ *    state between calls (calls are thread-safe).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; results are valid after the stream syncs.
+ *  - Arguments are validated on the host before anything is enqueued.  On an
+ *    error the function returns a non-zero pgkq_status and enqueues nothing.
+ *    A HIP launch error maps to PGKQ_ERR_HIP.  No C++ exception crosses this ABI.
+ *  - Device pointers must be 16-byte aligned.
+ *  - n_tokens == 0 is a valid no-op (outputs untouched, except that decode
+ *    attention writes zeros to `out` because an empty softmax has no weights).
+ *
+ * Code layout of one (sequence, kv-head) stream with room for `capacity` tokens
+ * (exactly pgkq_record_bytes() bytes per token slot):
+ *    P = b_main + b_angle bits per pair; joint code c_i = rc_i | (ac_i << b_main);
+ *    per token a code stream of (d/2) P bits, c_i at bits [P i, P i + P), LSB
+ *      first, in NC = (d/2) P / 32 uint32 words (bit q in word q/32, bit q%32);
+ *    then, with QJL, m/32 sign words (bit j of the sketch in word j/32, bit j%32);
+ *    word w of token t is stored at byte 4 (w capacity + t) of the stream;
+ *    with QJL a row of `capacity` fp16 residual norms follows the words.
+ *  Streams are stored back to back in [n_seq][n_kv] order, capacity * record
+ *  bytes each.
+ *
+ * Per-kv-head inputs, shared by all sequences:
+ *    signs    [n_kv][d]     int8, +1 / -1 (Rademacher vector of the transform)
+ *    perm     [n_kv][d]     uint16 channel order of step (0), or NULL = identity
+ *    codebook [n_kv][2L]    fp32, L = 2^b_main: L radius levels (ascending),
+ *                           L-1 thresholds (a radius r gets code #{j : T_j < r}),
+ *                           one unused pad; absolute radius units
+ *    S        [n_kv][m][d]  fp32 QJL projection, NULL iff qjl_m == 0
+ */
+#ifndef PGKQ_H
+#define PGKQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pgkq_status {
+  PGKQ_OK = 0,
+  PGKQ_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  PGKQ_ERR_SHAPE = 2,       /* a size is negative, inconsistent or out of range */
+  PGKQ_ERR_UNSUPPORTED = 3, /* parameter combination the library does not build */
+  PGKQ_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned          */
+  PGKQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+  PGKQ_ERR_HIP = 6          /* the HIP runtime reported an error                */
+} pgkq_status;
+
+typedef enum pgkq_dtype { PGKQ_F32 = 0, PGKQ_F16 = 1, PGKQ_BF16 = 2 } pgkq_dtype;
+
+typedef struct pgkq_params {
+  int32_t head_dim; /* d: 64 or 128                                              */
+  int32_t b_main;   /* radius code bits: 2, 3 or 4                              */
+  int32_t b_angle;  /* angle code bits: must equal b_main - 1                   */
+  int32_t qjl_m;    /* QJL sketch size: 0 (off) or head_dim                     */
+  int32_t hadamard; /* 1: randomized Hadamard transform; 0: identity transform  */
+                    /*    (the "without Hadamard" ablation)                     */
+} pgkq_params;
+
+/* Optional launch settings; a NULL pointer means all defaults. */
+typedef struct pgkq_launch_opts {
+  int32_t n_splits;  /* token splits per (sequence, kv-head); 0 = automatic      */
+  void* scan_start;  /* hipEvent_t recorded just before the token-scan kernel    */
+  void* scan_stop;   /* hipEvent_t recorded just after it (both NULL = none)    */
+} pgkq_launch_opts;
+
+/* Human-readable name of a status code (static string). */
+const char* pgkq_status_string(pgkq_status s);
+
+/* Library version string (static). */
+const char* pgkq_version(void);
+
+/* Bytes of one token slot of one stream (30 at d=64, b_main=3, QJL m=64; the
+ * record size of the "Bit budget" paragraph).  0 if the parameters are invalid. */
+size_t pgkq_record_bytes(const pgkq_params* p);
+
+/* Bytes of a code buffer holding n_streams streams of `capacity` slots. */
+size_t pgkq_codes_bytes(const pgkq_params* p, int64_t n_streams, int64_t capacity);
+
+/* Host routine.  Lloyd-Max quantizer of rho = (r / ||k||) sqrt(d/2) under the
+ * Beta(1, d/2 - 1) prior of r^2 / ||k||^2 (the codebook paragraph after "PGKQ
+ * pipeline": Lloyd-Max for the Beta prior, not refit on data).  Writes
+ * 2^b_main ascending levels and 2^b_main - 1 midpoint thresholds into HOST
+ * arrays, float64.  Iterates until no level moves by more than 1e-13. */
+pgkq_status pgkq_lloyd_max_beta(int32_t head_dim, int32_t b_main, double* levels_host,
+                                double* thresholds_host);
+
+/* Bytes of workspace pgkq_calibrate needs. */
+size_t pgkq_calibrate_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_kv,
+                                      int64_t n_tokens);
+
+/* Calibration over the keys about to be encoded (step (0) and the radius scale;
+ * the "PGKQ pipeline" starts from calibration keys):
+ *   K        [n_seq][n_kv][n_tokens][d] keys, dtype k_dtype (F32 or F16)
+ *   sumsq    out [n_kv][d] float64: per channel sum of k^2 over sequences and tokens
+ *   perm     out [n_kv][d] uint16: if reorder, channels sorted by descending sum of
+ *            squares (stable), interleaved [pi_0, pi_{d-1}, pi_1, pi_{d-2}, ...];
+ *            else the identity.  May be NULL when reorder == 0.
+ *   codebook out [n_kv][2L] fp32: the Lloyd-Max levels/thresholds times
+ *            s_h / sqrt(d/2), s_h = sqrt(sum_c sumsq[h][c] / (n_seq n_tokens)),
+ *            each product formed in float64 and rounded once to fp32.
+ * n_tokens must be >= 1.  The result is deterministic (fixed summation order). */
+pgkq_status pgkq_calibrate(const pgkq_params* p, const void* K, pgkq_dtype k_dtype,
+                           int64_t n_seq, int64_t n_kv, int64_t n_tokens, int32_t reorder,
+                           double* sumsq, uint16_t* perm, float* codebook, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Encode keys into the code buffer (steps (1)-(4)):
+ *   K      [n_seq][n_kv][n_tokens][d], dtype k_dtype (F32 or F16)
+ *   codes  [n_seq][n_kv] streams of `capacity` slots; tokens are written to slots
+ *          [token_offset, token_offset + n_tokens) of every stream, other slots
+ *          are left untouched (appending to a live cache).
+ * Decisions (radius and angle codes, residual norm) are taken in float64 on the
+ * exact transform of the key; the QJL projection is accumulated in fp32. */
+pgkq_status pgkq_encode(const pgkq_params* p, const void* K, pgkq_dtype k_dtype, int64_t n_seq,
+                        int64_t n_kv, int64_t n_tokens, const int8_t* signs, const uint16_t* perm,
+                        const float* codebook, const float* S, void* codes, int64_t capacity,
+                        int64_t token_offset, void* stream);
+
+/* Bytes of workspace pgkq_decode_attn / pgkq_estimate_logits need. */
+size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_q,
+                                   int64_t n_kv, int64_t n_tokens, const pgkq_launch_opts* opts);
+
+/* Decode attention over the compressed keys and fp16 values:
+ *   q     [n_seq][n_q][d], dtype q_dtype (F32, F16 or BF16); query head hq reads
+ *         kv-head hq / (n_q / n_kv); n_q / n_kv must be 1, 2, 4 or 8
+ *   codes as written by pgkq_encode, tokens [0, n_tokens) of each stream
+ *   V     [n_seq][n_kv][capacity][d] fp16
+ *   out   [n_seq][n_q][d] fp32 = sum_t softmax_t(scale * logit_t) V_t
+ *   softmax_scale <= 0 selects 1 / sqrt(d).
+ * The logit of token t is
+ *   sum_i level[rc_i] (q~[2i] cos thetahat[ac_i] + q~[2i+1] sin thetahat[ac_i])
+ *   + sqrt(pi/2)/m * nu_t * sum_j (S_h q~)_j (2 bit_tj - 1),
+ * with q~ the query through the kv-head's transform.  The token range is split
+ * across workgroups (flash-decoding); partial states are merged with a
+ * log-sum-exp merge.  Workspace: pgkq_decode_workspace_bytes(). */
+pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                             int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                             int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                             const float* codebook, const float* S, const void* codes,
+                             const void* V, float* out, float softmax_scale,
+                             const pgkq_launch_opts* opts, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* The attention-logit hook of the throughput paragraph: raw logits (estimates
+ * of <q, k_t>, no softmax scale) into logits [n_seq][n_q][n_tokens] fp32.  Same
+ * device code as the score step of pgkq_decode_attn.  Workspace as for decode. */
+pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                                 int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                 int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                                 const float* codebook, const float* S, const void* codes,
+                                 float* logits, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Bytes of workspace pgkq_fp16_decode_attn needs. */
+size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q,
+                                        int64_t n_kv, int64_t n_tokens,
+                                        const pgkq_launch_opts* opts);
+
+/* Uncompressed comparator: decode attention on an fp16 key cache (the FP16
+ * cache the pages take fidelity deltas against).
+ *   K16, V16 [n_seq][n_kv][capacity][d] fp16; q, out, scale as for decode. */
+pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q,
+                                  int64_t n_kv, int64_t n_tokens, int64_t capacity,
+                                  int32_t head_dim, const void* K16, const void* V16, float* out,
+                                  float softmax_scale, const pgkq_launch_opts* opts,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* PGKQ_H */

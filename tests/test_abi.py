@@ -1,0 +1,198 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes records and workspaces, builds the codebook on the host,
+and rejects every invalid argument before touching the device."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from compressed_cache_decode_pgkq_amd import _lib as L
+from compressed_cache_decode_pgkq_amd import api
+from oracle import codebook
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pgkq.h")
+
+A = 0x100000  # a 16-byte aligned stand-in pointer, never dereferenced (validation fails first)
+MIS = A + 8
+
+
+def _vp(x):
+    return ctypes.c_void_p(x)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pgkq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert len(names) >= 12
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings_and_version():
+    lib = L.lib()
+    for s in range(7):
+        assert lib.pgkq_status_string(s)
+    assert b"gfx950" in lib.pgkq_version()
+
+
+@pytest.mark.parametrize("prm,rb", [((64, 3, 2, 64), 30), ((64, 4, 3, 0), 28), ((128, 3, 2, 128), 58),
+                                    ((128, 4, 3, 128), 74), ((64, 2, 1, 64), 22), ((128, 3, 2, 0), 40)])
+def test_record_bytes(prm, rb):
+    p = api.PgkqParams(*prm)
+    assert api.pgkq_record_bytes(p) == rb
+    assert api.pgkq_codes_bytes(p, 24, 128) == 24 * 128 * rb
+    # the printed 128-token example: 92 160 bytes of keys for 24 heads
+    if prm == (64, 3, 2, 64):
+        assert api.pgkq_codes_bytes(p, 24, 128) == 92160
+
+
+@pytest.mark.parametrize("prm", [(96, 3, 2, 0), (64, 3, 3, 0), (64, 5, 4, 0), (64, 1, 0, 0),
+                                 (64, 3, 2, 32), (64, 3, 2, 64, 2)])
+def test_invalid_params_have_no_record(prm):
+    assert api.pgkq_record_bytes(api.PgkqParams(*prm)) == 0
+
+
+@pytest.mark.parametrize("d,b", [(64, 2), (64, 3), (64, 4), (128, 3), (128, 4), (16, 2)])
+def test_host_lloyd_max_matches_oracle(d, b):
+    lv, th = api.pgkq_lloyd_max_beta(d, b)
+    c, t = codebook.lloyd_max_beta(d, b)
+    np.testing.assert_allclose(lv, c, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(th, t, rtol=0, atol=1e-11)
+
+
+def test_host_lloyd_max_rejects():
+    lv = (ctypes.c_double * 16)()
+    th = (ctypes.c_double * 16)()
+    lib = L.lib()
+    assert lib.pgkq_lloyd_max_beta(64, 3, None, th) == L.PGKQ_ERR_NULL
+    assert lib.pgkq_lloyd_max_beta(3, 3, lv, th) == L.PGKQ_ERR_UNSUPPORTED
+    assert lib.pgkq_lloyd_max_beta(64, 0, lv, th) == L.PGKQ_ERR_UNSUPPORTED
+
+
+def _params(*prm):
+    return ctypes.byref(L.PgkqParams(*prm))
+
+
+def _encode(p=(64, 3, 2, 64, 1), K=A, kd=L.PGKQ_F32, n_seq=1, n_kv=2, n_tok=16, signs=A, perm=None,
+            cb=A, S=A, codes=A, cap=16, off=0):
+    return L.lib().pgkq_encode(_params(*p) if p else None, _vp(K) if K else None, kd, n_seq, n_kv,
+                               n_tok, _vp(signs) if signs else None, _vp(perm) if perm else None,
+                               _vp(cb) if cb else None, _vp(S) if S else None,
+                               _vp(codes) if codes else None, cap, off, None)
+
+
+def test_encode_validation():
+    assert _encode(p=None) == L.PGKQ_ERR_NULL
+    assert _encode(K=0) == L.PGKQ_ERR_NULL
+    assert _encode(S=0) == L.PGKQ_ERR_NULL            # QJL needs S
+    assert _encode(codes=0) == L.PGKQ_ERR_NULL
+    assert _encode(p=(96, 3, 2, 0, 1)) == L.PGKQ_ERR_UNSUPPORTED
+    assert _encode(p=(64, 3, 1, 64, 1)) == L.PGKQ_ERR_UNSUPPORTED
+    assert _encode(kd=L.PGKQ_BF16) == L.PGKQ_ERR_UNSUPPORTED
+    assert _encode(kd=7) == L.PGKQ_ERR_UNSUPPORTED
+    assert _encode(n_seq=0) == L.PGKQ_ERR_SHAPE
+    assert _encode(n_kv=70000) == L.PGKQ_ERR_SHAPE
+    assert _encode(n_tok=17) == L.PGKQ_ERR_SHAPE      # beyond capacity
+    assert _encode(off=1) == L.PGKQ_ERR_SHAPE
+    assert _encode(n_tok=-1) == L.PGKQ_ERR_SHAPE
+    assert _encode(cap=15, n_tok=8) == L.PGKQ_ERR_SHAPE  # odd capacity with QJL
+    assert _encode(K=MIS) == L.PGKQ_ERR_ALIGN
+    assert _encode(codes=MIS) == L.PGKQ_ERR_ALIGN
+    assert _encode(perm=MIS) == L.PGKQ_ERR_ALIGN
+    # zero tokens: valid no-op, nothing enqueued
+    assert _encode(n_tok=0) == L.PGKQ_OK
+    # no QJL: S may be NULL
+    assert _encode(p=(64, 4, 3, 0, 1), S=0, n_tok=0) == L.PGKQ_OK
+
+
+def _decode(p=(128, 3, 2, 128, 1), q=A, qd=L.PGKQ_BF16, n_seq=2, n_q=8, n_kv=2, n_tok=100, cap=128,
+            signs=A, perm=None, cb=A, S=A, codes=A, V=A, out=A, ws=A, wsb=1 << 30, n_splits=0):
+    o = L.PgkqLaunchOpts(n_splits, None, None)
+    return L.lib().pgkq_decode_attn(_params(*p), _vp(q) if q else None, qd, n_seq, n_q, n_kv, n_tok,
+                                    cap, _vp(signs), _vp(perm) if perm else None, _vp(cb),
+                                    _vp(S) if S else None, _vp(codes) if codes else None,
+                                    _vp(V) if V else None, _vp(out) if out else None, 0.0,
+                                    ctypes.byref(o), _vp(ws) if ws else None, wsb, None)
+
+
+def test_decode_validation():
+    assert _decode(q=0) == L.PGKQ_ERR_NULL
+    assert _decode(V=0) == L.PGKQ_ERR_NULL
+    assert _decode(out=0) == L.PGKQ_ERR_NULL
+    assert _decode(ws=0) == L.PGKQ_ERR_NULL
+    assert _decode(S=0) == L.PGKQ_ERR_NULL
+    assert _decode(n_q=6) == L.PGKQ_ERR_UNSUPPORTED   # group of 3
+    assert _decode(n_q=7) == L.PGKQ_ERR_SHAPE         # not a multiple of n_kv
+    assert _decode(n_q=32) == L.PGKQ_ERR_UNSUPPORTED  # group of 16
+    assert _decode(n_tok=129) == L.PGKQ_ERR_SHAPE
+    assert _decode(cap=127, n_tok=100) == L.PGKQ_ERR_SHAPE
+    assert _decode(qd=9) == L.PGKQ_ERR_UNSUPPORTED
+    assert _decode(V=MIS) == L.PGKQ_ERR_ALIGN
+    assert _decode(out=MIS) == L.PGKQ_ERR_ALIGN
+    assert _decode(wsb=16) == L.PGKQ_ERR_WORKSPACE
+    p = api.PgkqParams(128, 3, 2, 128)
+    need = api.pgkq_decode_workspace_bytes(p, 2, 8, 2, 100)
+    assert need > 0
+    assert _decode(wsb=need - 1) == L.PGKQ_ERR_WORKSPACE
+
+
+def test_logits_and_fp16_validation():
+    lib = L.lib()
+    st = lib.pgkq_estimate_logits(_params(64, 3, 2, 64, 1), _vp(A), L.PGKQ_F32, 1, 4, 4, 10, 16,
+                                  _vp(A), None, _vp(A), _vp(A), _vp(A), None, _vp(A), 1 << 20, None)
+    assert st == L.PGKQ_ERR_NULL
+    o = L.PgkqLaunchOpts(0, None, None)
+    st = lib.pgkq_fp16_decode_attn(_vp(A), L.PGKQ_F32, 1, 4, 4, 10, 16, 96, _vp(A), _vp(A), _vp(A),
+                                   0.0, ctypes.byref(o), _vp(A), 1 << 20, None)
+    assert st == L.PGKQ_ERR_UNSUPPORTED
+    st = lib.pgkq_fp16_decode_attn(_vp(A), L.PGKQ_F32, 1, 4, 4, 10, 16, 64, None, _vp(A), _vp(A),
+                                   0.0, ctypes.byref(o), _vp(A), 1 << 20, None)
+    assert st == L.PGKQ_ERR_NULL
+    st = lib.pgkq_fp16_decode_attn(_vp(A), L.PGKQ_F32, 1, 12, 4, 10, 16, 64, _vp(A), _vp(A), _vp(A),
+                                   0.0, ctypes.byref(o), _vp(A), 1 << 20, None)
+    assert st == L.PGKQ_ERR_UNSUPPORTED
+    need = lib.pgkq_fp16_decode_workspace_bytes(128, 16, 32, 8, 32768, ctypes.byref(o))
+    st = lib.pgkq_fp16_decode_attn(_vp(A), L.PGKQ_F32, 16, 32, 8, 32768, 32768, 128, _vp(A), _vp(A),
+                                   _vp(A), 0.0, ctypes.byref(o), _vp(A), need - 1, None)
+    assert need > 0 and st == L.PGKQ_ERR_WORKSPACE
+
+
+def test_calibrate_validation():
+    lib = L.lib()
+    p = _params(128, 3, 2, 128, 1)
+    need = lib.pgkq_calibrate_workspace_bytes(p, 16, 8, 32768)
+    assert need >= 8 * 128 * 8
+    args = dict(K=A, kd=L.PGKQ_F16, n_seq=16, n_kv=8, n_tok=32768, reorder=1, ss=A, perm=A, cb=A,
+                ws=A, wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.pgkq_calibrate(p, _vp(a["K"]) if a["K"] else None, a["kd"], a["n_seq"], a["n_kv"],
+                                  a["n_tok"], a["reorder"], _vp(a["ss"]),
+                                  _vp(a["perm"]) if a["perm"] else None, _vp(a["cb"]), _vp(a["ws"]),
+                                  a["wsb"], None)
+
+    assert call(K=0) == L.PGKQ_ERR_NULL
+    assert call(perm=0) == L.PGKQ_ERR_NULL
+    assert call(n_tok=0) == L.PGKQ_ERR_SHAPE
+    assert call(wsb=need - 1) == L.PGKQ_ERR_WORKSPACE
+    assert call(K=MIS) == L.PGKQ_ERR_ALIGN
+    assert call(kd=L.PGKQ_BF16) == L.PGKQ_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_grow_with_splits():
+    p = api.PgkqParams(128, 4, 3, 128)
+    w1 = api.pgkq_decode_workspace_bytes(p, 1, 32, 8, 131072, n_splits=1)
+    w256 = api.pgkq_decode_workspace_bytes(p, 1, 32, 8, 131072, n_splits=256)
+    assert w256 - w1 >= 32 * 256 * (128 + 4) * 4 - 256

@@ -1,0 +1,285 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+
+Bars (stated for the method): codes bit-exact except decision-boundary cases
+(classified in parity_util, fewer than 1e-5 of all code fields); logits within
+2e-3 * ||q|| * ||k|| absolute; attention outputs within 1e-3 max-abs.
+Decode parity runs on identical code buffers (packed by the oracle) so that an
+encoder boundary case cannot leak into the decoder comparison.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attn, layout
+from synth import CONFIGS
+
+from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev
+from parity_util import assert_code_parity, classify, merge_counts
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 1e-3
+LOGIT_TOL = 2e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    from compressed_cache_decode_pgkq_amd import _lib
+    _lib.lib()  # the HIP library must be built; no fallback exists
+
+
+def _api():
+    import compressed_cache_decode_pgkq_amd as api
+    return api
+
+
+SMALL = {
+    "c1": (CONFIGS["c1"], {}),
+    "c2a": (CONFIGS["c2a"].with_(n_seq=3), {}),
+    "c2b": (CONFIGS["c2b"].with_(n_seq=3), {}),
+    "c3": (CONFIGS["c3"].with_(n_seq=2, n_tokens=1000), {}),
+    "c4": (CONFIGS["c4"].with_(n_seq=2, n_tokens=700), {"reorder": True}),
+    "c5": (CONFIGS["c5"].with_(n_tokens=3000), {}),
+}
+
+
+def _gpu_encode(case, K=None):
+    api = _api()
+    dev = case.dev_inputs()
+    Kt = k_tensor(case.K if K is None else K)
+    codes = api.pgkq_encode(lib_params(case.p), Kt, dev["signs"], dev["perm"], dev["codebook"],
+                            dev["S"], capacity=case.cap)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy()
+
+
+def _code_counts(case, got):
+    f = case.oracle_fields()
+    counts = {}
+    n_seq, n_kv = case.K.shape[:2]
+    for b in range(n_seq):
+        for h in range(n_kv):
+            u = layout.unpack_stream(got[b, h], case.p, case.cap, case.T)
+            merge_counts(counts, classify(f[b][h], u, case.tables[h][1],
+                                          None if case.S is None else case.S[h], case.p))
+    return counts
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_encode_codes_match_oracle(name):
+    cfg, kw = SMALL[name]
+    case = Case(cfg, **kw)
+    got = _gpu_encode(case)
+    counts = _code_counts(case, got)
+    print(name, counts)
+    assert_code_parity(counts)
+    if counts["mismatch"] == 0:
+        assert np.array_equal(got, case.oracle_codes())
+
+
+def test_encode_without_hadamard():
+    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=500), hadamard=False)
+    counts = _code_counts(case, _gpu_encode(case))
+    print(counts)
+    assert_code_parity(counts)
+
+
+def test_encode_appends_at_token_offset():
+    api = _api()
+    cfg = CONFIGS["c2a"].with_(n_seq=2, n_tokens=200)
+    case = Case(cfg, capacity=256)
+    dev = case.dev_inputs()
+    p = lib_params(case.p)
+    codes = torch.zeros((2, cfg.n_kv, case.cap * layout.record_bytes(case.p)), dtype=torch.uint8,
+                        device="cuda:0")
+    # two appends: tokens [0, 77) then [77, 200)
+    for t0, t1 in ((0, 77), (77, 200)):
+        api.pgkq_encode(p, k_tensor(case.K[:, :, t0:t1]), dev["signs"], dev["perm"], dev["codebook"],
+                        dev["S"], codes=codes, capacity=case.cap, token_offset=t0)
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    assert np.array_equal(got, case.oracle_codes())
+
+
+@pytest.mark.parametrize("name", ["c1", "c2a", "c4"])
+def test_calibrate_matches_oracle(name):
+    api = _api()
+    cfg, kw = SMALL[name]
+    reorder = kw.get("reorder", False)
+    case = Case(cfg, **kw)
+    sumsq, perm, cb = api.pgkq_calibrate(lib_params(case.p), k_tensor(case.K), reorder=reorder)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(sumsq.cpu().numpy(), case.sumsq, rtol=1e-12)
+    if reorder:
+        assert np.array_equal(perm.cpu().numpy().view(np.uint16), case.perm.astype(np.uint16))
+    got = cb.cpu().numpy()
+    ulp = np.abs(np.spacing(case.cb.astype(np.float32)))
+    fin = np.isfinite(case.cb)
+    assert np.all(np.abs(got[fin] - case.cb[fin]) <= ulp[fin])
+    assert np.all(np.isinf(got[~fin]))
+
+
+def _logit_bound(case, b, hq):
+    G = case.cfg.n_q // case.cfg.n_kv
+    qn = np.linalg.norm(case.q[b, hq].astype(np.float64))
+    kn = np.linalg.norm(case.K[b, hq // G].astype(np.float64), axis=1)
+    return LOGIT_TOL * qn * kn
+
+
+def _check_decode(case, n_splits=0, q_override=None, q_dtype=None):
+    api = _api()
+    dev = case.dev_inputs()
+    p = lib_params(case.p)
+    q = case.q if q_override is None else q_override
+    qt = q_tensor(q, q_dtype or case.cfg.q_dtype)
+    codes = to_dev(case.oracle_codes())
+    out = api.pgkq_decode_attn(p, qt, codes, dev["V"], dev["signs"], dev["perm"], dev["codebook"],
+                               dev["S"], n_tokens=case.T, n_splits=n_splits)
+    lg = api.pgkq_estimate_logits(p, qt, codes, case.cfg.n_kv, case.cap, dev["signs"], dev["perm"],
+                                  dev["codebook"], dev["S"], n_tokens=case.T)
+    torch.cuda.synchronize()
+    ref, ref_lg = case.oracle_decode(q=q)
+    out = out.cpu().numpy()
+    lg = lg.cpu().numpy()
+    err = float(np.max(np.abs(out - ref))) if out.size else 0.0
+    n_seq, n_q = q.shape[:2]
+    worst = 0.0
+    for b in range(n_seq):
+        for hq in range(n_q):
+            bound = _logit_bound(case, b, hq)
+            worst = max(worst, float(np.max(np.abs(lg[b, hq] - ref_lg[b, hq]) / bound)) if case.T else 0)
+    print(f"decode max-abs {err:.3e}  logit err / bound {worst:.3e}")
+    assert err <= OUT_TOL
+    assert worst <= 1.0
+    return out
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("n_splits", [1, 0, 7])
+def test_decode_matches_oracle_on_identical_codes(name, n_splits):
+    cfg, kw = SMALL[name]
+    _check_decode(Case(cfg, **kw), n_splits=n_splits)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+def test_decode_group_sizes(group):
+    cfg = CONFIGS["c3"].with_(n_seq=2, n_kv=2, n_q=2 * group, n_tokens=600)
+    _check_decode(Case(cfg), n_splits=0)
+
+
+@pytest.mark.parametrize("qd", ["f32", "f16", "bf16"])
+def test_decode_query_dtypes(qd):
+    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=400))
+    q = case.q.astype(np.float16).astype(np.float32) if qd == "f16" else case.q
+    _check_decode(case, q_override=q, q_dtype=qd)
+
+
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 257, 1000])
+def test_decode_ragged_lengths(T):
+    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=1000), n_tokens=T, capacity=1024)
+    _check_decode(case, n_splits=0)
+    _check_decode(case, n_splits=3)
+
+
+def test_decode_empty_cache_gives_zeros():
+    api = _api()
+    case = Case(CONFIGS["c1"], n_tokens=0, capacity=128)
+    dev = case.dev_inputs()
+    out = torch.full((1, 24, 64), 7.0, device="cuda:0")
+    api.pgkq_decode_attn(lib_params(case.p), q_tensor(case.q, "f32"),
+                         torch.zeros((1, 24, 128 * 30), dtype=torch.uint8, device="cuda:0"),
+                         dev["V"], dev["signs"], None, dev["codebook"], dev["S"], n_tokens=0, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+def test_decode_without_hadamard():
+    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=500), hadamard=False)
+    _check_decode(case)
+
+
+def test_end_to_end_calibrate_encode_decode():
+    """GPU calibrate -> encode -> decode against oracle calibrate -> encode -> decode."""
+    api = _api()
+    cfg = CONFIGS["c4"].with_(n_seq=2, n_tokens=900)
+    case = Case(cfg, reorder=True)
+    p = lib_params(case.p)
+    Kt = k_tensor(case.K)
+    sumsq, perm, cb = api.pgkq_calibrate(p, Kt, reorder=True)
+    dev = case.dev_inputs()
+    codes = api.pgkq_encode(p, Kt, dev["signs"], perm, cb, dev["S"], capacity=case.cap)
+    out = api.pgkq_decode_attn(p, q_tensor(case.q, cfg.q_dtype), codes, dev["V"], dev["signs"], perm,
+                               cb, dev["S"], n_tokens=case.T)
+    torch.cuda.synchronize()
+    ref, _ = case.oracle_decode()
+    err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+    print("end-to-end max-abs", err)
+    assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("name", ["c2a", "c3"])
+def test_fp16_comparator_matches_oracle(name):
+    api = _api()
+    cfg, _ = SMALL[name]
+    case = Case(cfg)
+    n_seq, n_kv, T, d = case.K.shape
+    K16 = case.K.astype(np.float16)
+    Kp = np.zeros((n_seq, n_kv, case.cap, d), np.float16)
+    Kp[:, :, :T] = K16
+    dev = case.dev_inputs()
+    out = api.pgkq_fp16_decode_attn(q_tensor(case.q, cfg.q_dtype), to_dev(Kp), dev["V"], n_tokens=T)
+    torch.cuda.synchronize()
+    ref, _ = attn.fp16_attention(case.q, K16, case.V)
+    err = float(np.max(np.abs(out.cpu().numpy() - ref)))
+    print("fp16 comparator max-abs", err)
+    assert err <= OUT_TOL
+
+
+# ------------------------------------------------------------------ negative controls
+# A planted mistake lives in the oracle's data, on the CPU: the parity check
+# must notice it (the broken-cache control of the LCDF harness, applied here).
+
+def _decode_err(case, codes_np, tables=None, signs=None):
+    api = _api()
+    dev = case.dev_inputs()
+    p = lib_params(case.p)
+    out = api.pgkq_decode_attn(p, q_tensor(case.q, case.cfg.q_dtype), to_dev(case.oracle_codes()),
+                               dev["V"], dev["signs"], dev["perm"], dev["codebook"], dev["S"],
+                               n_tokens=case.T)
+    torch.cuda.synchronize()
+    n_seq, n_kv = case.K.shape[:2]
+    fields = [[layout.unpack_stream(codes_np[b, h], case.p, case.cap, case.T) for h in range(n_kv)]
+              for b in range(n_seq)]
+    ref, _ = attn.decode_cache(case.q, fields, case.V, tables or case.tables, case.S,
+                               case.signs if signs is None else signs, case.perm_arg, case.p)
+    return float(np.max(np.abs(out.cpu().numpy() - ref)))
+
+
+@pytest.mark.parametrize("mutation", ["radius_code", "sign_words", "rht_signs", "codebook"])
+def test_negative_controls_break_parity(mutation):
+    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=256))
+    good = case.oracle_codes()
+    assert _decode_err(case, good) <= OUT_TOL
+    bad = good.copy()
+    tables = None
+    signs = None
+    cap = case.cap
+    NC = layout.code_words(case.p)
+    words = bad[0, 0, : layout.n_words(case.p) * 4 * cap].view(np.uint32).reshape(-1, cap)
+    if mutation == "radius_code":
+        # move the heaviest-weight token's first radius code by one level
+        words[0, :] ^= 0x1
+    elif mutation == "sign_words":
+        words[NC:, :] = 0
+    elif mutation == "rht_signs":
+        signs = case.signs.copy()
+        signs[0, :8] *= -1
+    elif mutation == "codebook":
+        tables = [(lv[::-1].copy(), th) for lv, th in case.tables]
+    err = _decode_err(case, bad, tables=tables, signs=signs)
+    print(mutation, err)
+    assert err > OUT_TOL
