@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the PGKQ hot path on one MI355X.
+
+Workload: the GQA decode cache of 16 sequences x 8 kv-heads (32 query heads)
+x 32 768 tokens, head_dim 128, fp16 keys/values, bf16 queries, b_main 3 /
+b_angle 2 with a 128-bit QJL sketch; its 4 194 304 keys are also the bulk
+encode workload (with the channel reorder step).  Synthetic, seeded inputs
+(synth/), resident in HBM before the timed region.
+
+One step = the whole path: calibrate (channel sums, reorder, radius table) ->
+encode every key -> decode attention for every (sequence, query head) over the
+32k-token compressed cache (16 token splits).  A 512 MiB buffer is rewritten
+between encode and decode so that the decode does not read the freshly written
+codes out of the 256 MB Infinity Cache.  HIP events time each phase; the
+library records events around the decode scan kernel itself (the roofline
+figure).  The JSON line reports decode cache tokens/s as ``value``.
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP32_VALU_FMA_TFLOPS = 78.6    # 256 CU x 64 lanes x 2 flop x 2.4 GHz, unpacked fp32 FMA
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_scan_gqa32k_b16_traffic.json")
+SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/decode.hip",
+                "compressed_cache_decode_pgkq_amd/csrc/softmax_pv.hpp",
+                "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
+
+
+def scan_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in SCAN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def generate(cfg):
+    from synth import make_inputs
+    t = time.perf_counter()
+    inp = make_inputs(cfg)
+    log(f"[bench] generated {cfg.name} inputs in {time.perf_counter() - t:.1f} s")
+    return inp
+
+
+def cpu_baseline(cfg, inp, budget_s: float = 8.0):
+    """Time the float64 oracle on a bounded sample of the same workload."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attn, calibrate, codebook, encode
+
+    p = encode.Params(cfg.head_dim, cfg.b_main, cfg.b_angle, cfg.qjl_m)
+    G = cfg.n_q // cfg.n_kv
+    c, t = codebook.lloyd_max_beta(cfg.head_dim, cfg.b_main)
+    res = {}
+    with threadpool_limits(limits=1):
+        # decode: whole streams (32 768 tokens, the G query heads of the kv-head)
+        done_th, el = 0, 0.0
+        enc_keys, enc_el = 0, 0.0
+        n_streams = 0
+        while el < budget_s and n_streams < cfg.n_seq * cfg.n_kv:
+            b, h = divmod(n_streams, cfg.n_kv)
+            K = inp["K"][b, h]
+            ss = calibrate.channel_sumsq(K)
+            lv, th = codebook.scaled_table(c, t, calibrate.head_scale(ss, len(K)), cfg.head_dim)
+            t0 = time.perf_counter()
+            f = encode.encode_keys(K, inp["signs"][h], None, lv, th, inp["S"][h], p)
+            enc_el += time.perf_counter() - t0
+            enc_keys += len(K)
+            t0 = time.perf_counter()
+            for g in range(G):
+                s = attn.analytic_logits(inp["q"][b, h * G + g], f, lv, inp["S"][h], inp["signs"][h],
+                                         None, p)
+                attn.attend(s, inp["V"][b, h], 1.0 / math.sqrt(cfg.head_dim))
+            el += time.perf_counter() - t0
+            done_th += len(K)
+            n_streams += 1
+    # token-heads/s -> cache tokens/s (a cache token spans all n_kv kv-heads)
+    res["decode"] = {"value": done_th / el / cfg.n_kv, "unit": "cache tokens/s", "cores": 1,
+                     "kind": "oracle",
+                     "sample": f"{n_streams} streams x {cfg.n_tokens} tokens x {G} query heads "
+                               f"(decode of oracle-encoded codes, float64, {el:.1f} s)"}
+    res["encode"] = {"value": enc_keys / enc_el, "unit": "keys/s", "cores": 1, "kind": "oracle",
+                     "sample": f"{enc_keys} keys ({enc_el:.1f} s)"}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": args.steps}))
+        return
+
+    import compressed_cache_decode_pgkq_amd as api
+    from synth import CONFIGS
+
+    cfg = CONFIGS["c3"]           # decode workload
+    ecfg = CONFIGS["c4"]          # the same keys, encoded with the reorder step
+    inp = generate(cfg)
+    p = api.PgkqParams(cfg.head_dim, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
+    n_seq, n_kv, T, d = inp["K"].shape
+    K = torch.from_numpy(inp["K"]).to(dev)
+    V = torch.from_numpy(inp["V"]).to(dev)
+    q = torch.from_numpy(inp["q"]).to(torch.bfloat16).to(dev)
+    signs = torch.from_numpy(inp["signs"]).to(dev)
+    S = torch.from_numpy(inp["S"]).to(dev)
+    rb = api.pgkq_record_bytes(p)
+    codes = torch.zeros((n_seq, n_kv, T * rb), dtype=torch.uint8, device=dev)
+    out = torch.empty((n_seq, cfg.n_q, d), dtype=torch.float32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    ws = torch.empty(api.pgkq_decode_workspace_bytes(p, n_seq, cfg.n_q, n_kv, T, cfg.n_splits),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: K {K.numel() * 2 / 2**30:.2f} GiB, V {V.numel() * 2 / 2**30:.2f} GiB, "
+        f"codes {codes.numel() / 2**20:.1f} MiB")
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        _, perm, cb = api.pgkq_calibrate(p, K, reorder=ecfg.reorder)
+        if ev:
+            ev[1].record()
+        api.pgkq_encode(p, K, signs, perm, cb, S, codes=codes, capacity=T)
+        if ev:
+            ev[2].record()
+        flush.fill_(1)
+        if ev:
+            ev[3].record()
+        api.pgkq_decode_attn(p, q, codes, V, signs, perm, cb, S, n_splits=cfg.n_splits, out=out,
+                             workspace=ws, events=(ev[5], ev[6]) if ev else None)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[E() for _ in range(7)] for _ in range(args.steps)]
+    for e in evs:  # torch creates the HIP event on first record; the library re-records 5 and 6
+        e[5].record()
+        e[6].record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ph = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[3].elapsed_time(e[4]),
+                    e[5].elapsed_time(e[6])] for e in evs])  # ms
+    cal_ms, enc_ms, dec_ms, scan_ms = (float(np.median(ph[:, k])) for k in range(4))
+    scan_mean = float(np.mean(ph[:, 3]))
+
+    token_heads = n_seq * n_kv * T
+    alg_bytes = token_heads * (rb + 2 * d)
+    cache_tokens = n_seq * T
+    value = cache_tokens / (dec_ms * 1e-3)
+    achieved = alg_bytes / (scan_mean * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == scan_source_hash():
+            traffic = tr.get("bytes_per_launch")
+    n_keys = n_seq * n_kv * T
+    enc_flops = n_keys * 2.0 * cfg.qjl_m * d
+    result = {
+        "metric": "decode-attn cache tokens/s/GPU + % HBM roofline; PGKQ encode keys/s",
+        "value": value,
+        "unit": "cache tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; keys with log-normal channel scales and 4 outlier channels x10)",
+        "config": {
+            "workload": "GQA decode 32q/8kv, head_dim 128, 32768-token cache, batch 16, "
+                        "b_main 3 / b_angle 2, QJL m 128, 16 token splits; encode of its "
+                        "4194304 fp16 keys with the channel reorder step",
+            "n_seq": n_seq, "n_q": cfg.n_q, "n_kv": n_kv, "n_tokens": T, "head_dim": d,
+            "b_main": cfg.b_main, "b_angle": cfg.b_angle, "qjl_m": cfg.qjl_m,
+            "n_splits": cfg.n_splits, "record_bytes": rb,
+        },
+        "phases_ms": {"calibrate": cal_ms, "encode": enc_ms, "decode_attn": dec_ms,
+                      "decode_scan_kernel": scan_ms},
+        "decode": {"cache_tokens_per_s": value, "token_heads_per_s": token_heads / (dec_ms * 1e-3),
+                   "algorithmic_bytes": alg_bytes,
+                   "gbs_whole_call": alg_bytes / (dec_ms * 1e-3) / 1e9},
+        "encode": {"keys_per_s": n_keys / (enc_ms * 1e-3),
+                   "keys_per_s_with_calibrate": n_keys / ((enc_ms + cal_ms) * 1e-3),
+                   "hbm_gbs": n_keys * (2 * d + rb) / (enc_ms * 1e-3) / 1e9,
+                   "projection_tflops": enc_flops / (enc_ms * 1e-3) / 1e12,
+                   "roofline": {"bound": "alu", "achieved": enc_flops / (enc_ms * 1e-3) / 1e12,
+                                "peak": FP32_VALU_FMA_TFLOPS, "unit": "TFLOP/s",
+                                "frac": enc_flops / (enc_ms * 1e-3) / 1e12 / FP32_VALU_FMA_TFLOPS,
+                                "traffic": None}},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean},
+    }
+    if not args.no_cpu_baseline:
+        cb_res = cpu_baseline(cfg, inp)
+        result["cpu_baseline"] = cb_res["decode"]
+        result["cpu_baseline_encode"] = cb_res["encode"]
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
