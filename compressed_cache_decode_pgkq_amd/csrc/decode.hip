@@ -29,6 +29,17 @@ namespace {
 
 constexpr int kScanThreads = 256;
 constexpr int kScanWaves = kScanThreads / kWave;
+// waves per SIMD the register allocator must leave room for
+#ifndef PGKQ_SCAN_MIN_WAVES
+#define PGKQ_SCAN_MIN_WAVES 2
+#endif
+constexpr int kScanMinWavesPerEU = PGKQ_SCAN_MIN_WAVES;
+// table lookups issued per scheduling group of the score loop
+#ifndef PGKQ_PAIR_GROUP
+#define PGKQ_PAIR_GROUP 8
+#endif
+constexpr int kPairGroup = PGKQ_PAIR_GROUP;
+
 
 // ------------------------------------------------------------------ query prep
 
@@ -119,7 +130,7 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* cw, int i) {
 }
 
 template <int D, int BM, bool QJL, int G, bool LOGITS>
-__global__ void __launch_bounds__(kScanThreads)
+__global__ void __launch_bounds__(kScanThreads, kScanMinWavesPerEU)
 decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half* __restrict__ V) {
   using SS = ScanShape<D, BM, G>;
   constexpr int N = SS::N, BA = SS::BA, P = SS::P, L = SS::L, A = SS::A, NCODES = SS::NCODES;
@@ -144,64 +155,96 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   const float* lv = a.codebook + size_t(h) * 2 * L;
   const float* prep0 = a.prep + (size_t(b) * a.n_q + size_t(h) * G) * pl.stride();
 
-  // ---- tables
-  if constexpr (JOINT) {
-    for (int e = tid; e < N * NCODES * G; e += kScanThreads) {
-      const int g = e % G;
-      const int code = (e / G) % NCODES;
-      const int i = e / (G * NCODES);
-      const int rc = code & (L - 1), ac = code >> BM;
-      s_tab[e] = lv[rc] * prep0[size_t(g) * pl.stride() + pl.off_lut() + i * A + ac];
-    }
-  } else {
-    for (int e = tid; e < N * A * G; e += kScanThreads) {
-      const int g = e % G;
-      const int ia = e / G;  // i * A + ac
-      s_tab[e] = prep0[size_t(g) * pl.stride() + pl.off_lut() + ia];
-    }
-    for (int e = tid; e < L; e += kScanThreads) s_tab[N * A * G + e] = lv[e];
-  }
-  if constexpr (QJL) {
-    const float kappa = 1.2533141373155003f / float(M);  // sqrt(pi/2) / m
-    for (int e = tid; e < NQT; e += kScanThreads) {
-      const int g = e % G;
-      const int nib = (e / G) & 15;
-      const int k = e / (G * 16);
-      const float* sq = prep0 + size_t(g) * pl.stride() + pl.off_sq() + 4 * k;
-      float v = 0.f;
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) v += ((nib >> jb) & 1) ? sq[jb] : -sq[jb];
-      s_qt[e] = kappa * v;
-    }
-  }
-  __syncthreads();
-
   const int64_t t_begin = int64_t(split) * a.tokens_per_split;
   const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
   const uint8_t* cbase = codes + size_t(stream) * a.stream_bytes;
-  const uint32_t* rows = reinterpret_cast<const uint32_t*>(cbase);
-  const uint16_t* nurow = reinterpret_cast<const uint16_t*>(cbase + size_t(4) * NW * a.capacity);
-  const __half* vbase = V + size_t(stream) * a.capacity * D;
+  // buffer ranges: the whole code stream, and this stream's V rows [0, t_end)
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, static_cast<uint32_t>(a.stream_bytes));
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
+  const uint32_t nu_off = 4u * NW * static_cast<uint32_t>(a.capacity);
+  const uint32_t row_bytes = 4u * static_cast<uint32_t>(a.capacity);
 
   SoftmaxPV<D, G, kScanWaves> sm;
   sm.init(tid);
   const int lane = sm.lane, wave = sm.wave;
 
+  // Per chunk of 64 tokens, every load of the chunk (code words, norms, V rows)
+  // is issued at its start; V is consumed only after the score, so its latency
+  // hides behind the table lookups.
+  uint32_t cw[NW];
+  float nu = 0.f;
+  typename SoftmaxPV<D, G, kScanWaves>::VChunk vc;
+  // lanes past the split end read neighbouring (or, past the stream, zero)
+  // words; their scores are masked
+  auto load_codes = [&](int64_t c) {
+    const uint32_t t4 = static_cast<uint32_t>(c + lane) * 4u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cw[w] = buf_load_b32(crs, t4 + w * row_bytes);
+    if constexpr (QJL) nu = half_bits_to_float(buf_load_b16(crs, nu_off + t4 / 2));
+  };
+
+  // ---- tables: one thread per (pair, query head)
+  {
+    float lvr[L];
+#pragma unroll
+    for (int r = 0; r < L; ++r) lvr[r] = lv[r];
+    for (int ig = tid; ig < N * G; ig += kScanThreads) {
+      const int i = ig / G, g = ig % G;
+      const float* lut = prep0 + size_t(g) * pl.stride() + pl.off_lut() + i * A;
+      float lt[A];
+#pragma unroll
+      for (int ac = 0; ac < A; ++ac) lt[ac] = lut[ac];
+      if constexpr (JOINT) {
+#pragma unroll
+        for (int code = 0; code < NCODES; ++code)
+          s_tab[(i * NCODES + code) * G + g] = lvr[code & (L - 1)] * lt[code >> BM];
+      } else {
+#pragma unroll
+        for (int ac = 0; ac < A; ++ac) s_tab[(i * A + ac) * G + g] = lt[ac];
+      }
+    }
+    if constexpr (!JOINT) {
+      if (tid < L) s_tab[N * A * G + tid] = lvr[tid];
+    }
+  }
+  if constexpr (QJL) {
+    const float kappa = 1.2533141373155003f / float(M);  // sqrt(pi/2) / m
+    for (int kg = tid; kg < (M / 4) * G; kg += kScanThreads) {
+      const int k = kg / G, g = kg % G;
+      const float* sq = prep0 + size_t(g) * pl.stride() + pl.off_sq() + 4 * k;
+      const float q0 = sq[0], q1 = sq[1], q2 = sq[2], q3 = sq[3];
+#pragma unroll
+      for (int nib = 0; nib < 16; ++nib) {
+        const float v = ((nib & 1) ? q0 : -q0) + ((nib & 2) ? q1 : -q1) + ((nib & 4) ? q2 : -q2) +
+                        ((nib & 8) ? q3 : -q3);
+        s_qt[(k * 16 + nib) * G + g] = kappa * v;
+      }
+    }
+  }
+  __syncthreads();
+
   for (int64_t c0 = t_begin + int64_t(wave) * kWave; c0 < t_end; c0 += kScanThreads) {
     const int64_t t = c0 + lane;
     const bool valid = t < t_end;
-    uint32_t cw[NW];
-#pragma unroll
-    for (int w = 0; w < NW; ++w) cw[w] = valid ? rows[size_t(w) * a.capacity + t] : 0u;
-    float nu = 0.f;
-    if constexpr (QJL) nu = valid ? half_bits_to_float(nurow[t]) : 0.f;
+    load_codes(c0);
+    if constexpr (!LOGITS) sm.load_v(vc, c0, vrs);
 
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = 0.f;
 #pragma unroll
     for (int i = 0; i < N; ++i) {
+      // bound the work in flight (registers): the code words of each group of
+      // 8 pairs are pinned at the group's start, so neither their bit-field
+      // extracts nor their table reads are hoisted above it
+      if ((i % kPairGroup) == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) pin_reg(s[g]);
+#pragma unroll
+        for (int w = (P * i) / 32; w <= (P * (i + kPairGroup) - 1) / 32 && w < NC; ++w) pin_reg(cw[w]);
+      }
       const uint32_t code = code_at<P>(cw, i);
       float e[G];
       if constexpr (JOINT) {
@@ -221,6 +264,11 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       for (int g = 0; g < G; ++g) qs[g] = 0.f;
 #pragma unroll
       for (int k = 0; k < M / 4; ++k) {
+        if ((k % kPairGroup) == 0) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) pin_reg(qs[g]);
+          pin_reg(cw[NC + (k >> 3)]);
+        }
         const uint32_t nib = (cw[NC + (k >> 3)] >> (4 * (k & 7))) & 15u;
         float e[G];
         lds_fetch<G>(&s_qt[(k * 16 + nib) * G], e);
@@ -238,7 +286,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
           a.logits[(size_t(b) * a.n_q + size_t(h) * G + g) * a.n_tokens + t] = s[g];
       }
     } else {
-      sm.chunk(s, valid, a.scale_log2, c0, t_end, vbase, &s_p[wave][0][0]);
+      sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0]);
     }
   }
   if constexpr (!LOGITS) {

@@ -11,6 +11,38 @@ namespace pgkq {
 
 constexpr int kWave = 64;
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer access: a 128-bit resource (base, byte size) and 32-bit offsets
+// in a VGPR.  Reads at offsets at or beyond the size return zero (the buffer
+// unit's range check), so tail rows need no clamping.  The cache-kind bits
+// request non-temporal (streaming) loads: the cache is read once.
+constexpr int kLoadStream = 2;  // CDNA3/4 cache policy: NT
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, kLoadStream));
+}
+__device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, kLoadStream));
+}
+__device__ __forceinline__ uint16_t buf_load_b16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kLoadStream));
+}
+
+// Compiler-only fence: emits no instruction, but no memory access is moved
+// across it and it closes a scheduling region.  Used to keep the scheduler
+// from hoisting every LDS table read of a long unrolled loop (register
+// pressure).
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
+// Ties a register value to the current program point (emits nothing): work
+// derived from it cannot be hoisted above this line.
+__device__ __forceinline__ void pin_reg(uint32_t& v) { asm volatile("" : "+v"(v)::"memory"); }
+__device__ __forceinline__ void pin_reg(float& v) { asm volatile("" : "+v"(v)::"memory"); }
+
 __device__ __forceinline__ float load_f(const void* p, int dtype, int64_t i) {
   if (dtype == DT_F32) return static_cast<const float*>(p)[i];
   if (dtype == DT_F16) return __half2float(static_cast<const __half*>(p)[i]);
@@ -66,6 +98,24 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne_sat(double x) {
   }
   return static_cast<uint16_t>(sign | out);
 }
+
+// Wave-uniform maximum: DPP reductions inside each row of 16 lanes, then the
+// four row results through readlane (no LDS traffic).
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// 2^x with the hardware approximation (inputs are <= 0 here; results below the
+// smallest normal flush to zero, which a softmax weight may do).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {

@@ -38,13 +38,16 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
   const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
   const __half* kbase = K + size_t(stream) * a.capacity * D;
-  const __half* vbase = V + size_t(stream) * a.capacity * D;
+  const __amdgpu_buffer_rsrc_t vrs =
+      make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
 
   SoftmaxPV<D, G, kWaves> sm;
   sm.init(tid);
   for (int64_t c0 = t_begin + int64_t(sm.wave) * kWave; c0 < t_end; c0 += kThreads) {
     const int64_t t = c0 + sm.lane;
     const bool valid = t < t_end;
+    typename SoftmaxPV<D, G, kWaves>::VChunk vc;
+    sm.load_v(vc, c0, vrs);
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) s[g] = 0.f;
@@ -65,7 +68,7 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
         }
       }
     }
-    sm.chunk(s, valid, a.scale_log2, c0, t_end, vbase, &s_p[sm.wave][0][0]);
+    sm.chunk(s, valid, a.scale_log2, vc, &s_p[sm.wave][0][0]);
   }
   __syncthreads();
   sm.finish(s_main, tid, a.n_splits, split, a.out, a.partial, size_t(b) * a.n_q + size_t(h) * G);

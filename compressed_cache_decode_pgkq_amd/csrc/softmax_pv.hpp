@@ -61,45 +61,65 @@ struct SoftmaxPV {
     }
   }
 
-  // s: raw scores of token c0 + lane (ignored when !valid); p_row: this
-  // wavefront's [64][G] LDS rows; vbase: V of the stream.
+  // V rows of one chunk held in registers: row it*TPI + slot, channels
+  // dblk*8 .. dblk*8+7.  `vr` covers the split's rows [0, t_end) of the stream
+  // (buffer range), so rows past the split end read as zeros; their weight is
+  // zero as well.
+  struct VChunk {
+    u32x4 r[kWave / TPI];
+  };
+
+  __device__ __forceinline__ void load_v(VChunk& vc, int64_t c0, __amdgpu_buffer_rsrc_t vr) const {
+    const uint32_t base = static_cast<uint32_t>(c0 + slot) * (D * 2) + dblk * 16;
+#pragma unroll
+    for (int it = 0; it < kWave / TPI; ++it) vc.r[it] = buf_load_b128(vr, base + it * TPI * D * 2);
+  }
+
+  // s: raw scores of token c0 + lane (ignored when !valid); p_rows: this
+  // wavefront's [64][G] LDS rows.
   __device__ __forceinline__ void chunk(const float (&s)[G], bool valid, float scale_log2,
-                                        int64_t c0, int64_t t_end, const __half* __restrict__ vbase,
-                                        float* p_rows) {
+                                        const VChunk& vc, float* p_rows) {
+    float pv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float z = valid ? s[g] * scale_log2 : -INFINITY;
-      const float cmax = wave_max(z);
-      const float mnew = fmaxf(m_run[g], cmax);
-      const float alpha = exp2f(m_run[g] - mnew);  // m_run = -inf gives 0
-      const float p = valid ? exp2f(z - mnew) : 0.f;
-      l_lane[g] = l_lane[g] * alpha + p;
+      const float mnew = fmaxf(m_run[g], wave_max_uniform(z));
+      if (mnew > m_run[g]) {  // wave-uniform: rescale only when the maximum grows
+        const float alpha = fast_exp2(m_run[g] - mnew);  // m_run = -inf gives 0
+        l_lane[g] *= alpha;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[g][k] *= alpha;
-      m_run[g] = mnew;
-      p_rows[lane * G + g] = p;
+        for (int k = 0; k < 8; ++k) o[g][k] *= alpha;
+        m_run[g] = mnew;
+      }
+      pv[g] = valid ? fast_exp2(z - m_run[g]) : 0.f;
+      l_lane[g] += pv[g];
+    }
+    if constexpr (G == 1) {
+      p_rows[lane] = pv[0];
+    } else if constexpr (G == 2) {
+      *reinterpret_cast<float2*>(p_rows + lane * 2) = make_float2(pv[0], pv[1]);
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; g += 4)
+        *reinterpret_cast<float4*>(p_rows + lane * G + g) = make_float4(pv[g], pv[g + 1], pv[g + 2], pv[g + 3]);
     }
     wave_lds_sync();
-#pragma unroll 4
+#pragma unroll
     for (int it = 0; it < kWave / TPI; ++it) {
+      if ((it & 3) == 0) sched_fence();  // at most 4 weight rows read ahead
       const int r = it * TPI + slot;
-      const int64_t tt = c0 + r;
-      if (tt < t_end) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(vbase + size_t(tt) * D + dblk * 8);
-        const __half2* hv = reinterpret_cast<const __half2*>(&raw);
-        float vf[8];
+      __half2 hv[4];
+      __builtin_memcpy(hv, &vc.r[it], sizeof(hv));
+      float pp[G];
+      lds_fetch<G>(p_rows + r * G, pp);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float2 f2 = __half22float2(hv[k]);
-          vf[2 * k] = f2.x;
-          vf[2 * k + 1] = f2.y;
+      for (int k = 0; k < 4; ++k) {
+        const float2 f2 = __half22float2(hv[k]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          o[g][2 * k] = fmaf(pp[g], f2.x, o[g][2 * k]);
+          o[g][2 * k + 1] = fmaf(pp[g], f2.y, o[g][2 * k + 1]);
         }
-        float pp[G];
-        lds_fetch<G>(p_rows + r * G, pp);
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int k = 0; k < 8; ++k) o[g][k] = fmaf(pp[g], vf[k], o[g][k]);
       }
     }
     wave_lds_sync();
