@@ -4,8 +4,8 @@
 // per-head scale of the Lloyd-Max radius table.
 //
 // Two kernels, deterministic (fixed summation order, no atomics):
-//   calib_partial   one workgroup per (chunk of key rows, kv-head): float64 sums
-//                   of squares per channel into a workspace row;
+//   calib_partial   one workgroup per (chunk of token rows, kv-head, sequence):
+//                   float64 sums of squares per channel into a workspace row;
 //   calib_finalize  one workgroup per kv-head: sums the chunk rows in order,
 //                   derives s_h = sqrt(mean ||k||^2), scales the unit Lloyd-Max
 //                   table by s_h / sqrt(d/2) (float64 product, one rounding to
@@ -20,31 +20,51 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D>
+// One workgroup per (chunk of rows_per_chunk token rows, kv-head, sequence):
+// 16-byte loads, EPT consecutive channels per thread, float64 sums.
+template <int D, int ESIZE>
 __global__ void __launch_bounds__(kThreads) calib_partial_kernel(CalibArgs a) {
-  constexpr int PH = kThreads / D;  // row phases per workgroup
+  constexpr int EPT = 16 / ESIZE;        // elements per 16-byte load
+  constexpr int TPR = D / EPT;           // threads per row
+  constexpr int RPP = kThreads / TPR;    // rows per pass
   const int tid = threadIdx.x;
-  const int c = tid % D, ph = tid / D;
-  const int64_t ch = blockIdx.x;
+  const int cg = tid % TPR, rp = tid / TPR;
+  const int64_t tc = blockIdx.x;
   const int h = blockIdx.y;
-  const int64_t total = a.n_seq * a.n_tokens;
-  const int64_t r0 = ch * a.rows_per_chunk;
-  const int64_t r1 = min<int64_t>(r0 + a.rows_per_chunk, total);
-  double acc = 0.0;
-  for (int64_t r = r0 + ph; r < r1; r += PH) {
-    const int64_t bb = r / a.n_tokens, t = r % a.n_tokens;
-    const int64_t idx = ((bb * a.n_kv + h) * a.n_tokens + t) * D + c;
-    const double v = double(load_f(a.K, a.k_dtype, idx));
-    acc += v * v;
-  }
-  __shared__ double s_acc[kThreads];
-  s_acc[tid] = acc;
-  __syncthreads();
-  if (tid < D) {
-    double s = 0.0;
+  const int64_t b = blockIdx.z;
+  const int64_t t0 = tc * a.rows_per_chunk;
+  const int64_t t1 = min<int64_t>(t0 + a.rows_per_chunk, a.n_tokens);
+  const uint8_t* base = static_cast<const uint8_t*>(a.K) +
+                        ((b * a.n_kv + h) * a.n_tokens) * int64_t(D) * ESIZE + cg * 16;
+  double acc[EPT];
 #pragma unroll
-    for (int p = 0; p < PH; ++p) s += s_acc[p * D + tid];
-    a.partial[(size_t(h) * a.n_chunks + ch) * D + tid] = s;
+  for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
+  for (int64_t t = t0 + rp; t < t1; t += RPP) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(base + t * int64_t(D) * ESIZE);
+    if constexpr (ESIZE == 2) {
+      const __half2* hv = reinterpret_cast<const __half2*>(&raw);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float2 f = __half22float2(hv[k]);
+        acc[2 * k] += double(f.x) * double(f.x);
+        acc[2 * k + 1] += double(f.y) * double(f.y);
+      }
+    } else {
+      const float* fv = reinterpret_cast<const float*>(&raw);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += double(fv[k]) * double(fv[k]);
+    }
+  }
+  __shared__ double s_acc[RPP][D];
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) s_acc[rp][cg * EPT + e] = acc[e];
+  __syncthreads();
+  for (int c = tid; c < D; c += kThreads) {
+    double s = 0.0;
+#pragma unroll 8
+    for (int r = 0; r < RPP; ++r) s += s_acc[r][c];
+    const int64_t chunk = b * a.chunks_per_seq + tc;  // chunks of one head, in (b, tc) order
+    a.partial[(size_t(h) * a.n_chunks + chunk) * D + c] = s;
   }
 }
 
@@ -55,8 +75,17 @@ __global__ void __launch_bounds__(D) calib_finalize_kernel(CalibArgs a) {
   __shared__ double s_ss[D];
   __shared__ int s_pi[D];
   __shared__ double s_sigma;
-  double s = 0.0;
-  for (int64_t ch = 0; ch < a.n_chunks; ++ch) s += a.partial[(size_t(h) * a.n_chunks + ch) * D + c];
+  // eight interleaved partial sums (independent loads in flight), combined in
+  // a fixed order: the result does not depend on scheduling
+  double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const double* src = a.partial + size_t(h) * a.n_chunks * D + c;
+  int64_t ch = 0;
+  for (; ch + 8 <= a.n_chunks; ch += 8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) part[k] += src[(ch + k) * D];
+  }
+  for (int k = 0; ch < a.n_chunks; ++ch, ++k) part[k] += src[ch * D];
+  double s = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
   s_ss[c] = s;
   a.sumsq[size_t(h) * D + c] = s;
   __syncthreads();
@@ -93,8 +122,12 @@ __global__ void __launch_bounds__(D) calib_finalize_kernel(CalibArgs a) {
 
 template <int D>
 hipError_t calib_t(const CalibArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((calib_partial_kernel<D>), dim3(unsigned(a.n_chunks), unsigned(a.n_kv)),
-                     dim3(kThreads), 0, s, a);
+  const dim3 grid(unsigned(a.chunks_per_seq), unsigned(a.n_kv), unsigned(a.n_seq));
+  if (a.k_dtype == DT_F32) {
+    hipLaunchKernelGGL((calib_partial_kernel<D, 4>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((calib_partial_kernel<D, 2>), grid, dim3(kThreads), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((calib_finalize_kernel<D>), dim3(unsigned(a.n_kv)), dim3(D), 0, s, a);

@@ -5,7 +5,7 @@
 // Lloyd-Max radius code and uniform-grid angle code, optional QJL residual
 // sketch (sign bits of S_h eps~ plus an fp16 residual norm).
 //
-// One workgroup (4 wavefronts) encodes a tile of 64 keys of one (sequence,
+// A workgroup (4 wavefronts) walks a run of 64-key tiles of one (sequence,
 // kv-head) stream:
 //   * the key tile is staged in LDS with 16-byte coalesced loads;
 //   * each key is spread over 4 adjacent lanes (d/4 channels each) as float64;
@@ -16,9 +16,14 @@
 //     x^2 + y^2 against d T_j^2);
 //   * the residual eps~ and its norm stay in float64; the norm is rounded once
 //     to fp16;
-//   * the QJL projection runs lane-per-key: each wavefront owns a quarter of the
-//     m sketch rows, so the S_h addresses are wave-uniform and every S value
-//     read serves 64 keys; accumulation is fp32;
+//   * the QJL projection U = E S_h^T (64 keys x m rows, contraction over d) runs
+//     on the matrix cores: each operand is split into an fp16 high part and an
+//     fp16 remainder (the residual row first scaled by a power of two, which
+//     leaves every sign unchanged), and hi*hi + hi*lo + lo*hi accumulate in
+//     fp32 (about 22 significant bits per product).  S_h is split once per
+//     workgroup and kept in registers; each wavefront owns 32 sketch rows, so
+//     one ballot over a 32x32 accumulator block yields the sign words of 32
+//     keys;
 //   * codes are packed per token in LDS and stored as one coalesced 256-byte
 //     row segment per code word.
 #include "device_common.hpp"
@@ -29,15 +34,26 @@ namespace {
 
 constexpr int kTile = 64;
 constexpr int kThreads = 256;
+constexpr int kTilesPerBlock = 16;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int D>
 struct EncodeSmem {
-  static constexpr int EST = D + 4;  // fp32 residual row stride (bank spread)
-  static constexpr int kRawBytes = kTile * D * 4 > kTile * EST * 4 ? kTile * D * 4 : kTile * EST * 4;
+  static constexpr int EST = D + 8;  // fp16 residual row stride (bank spread)
+  static constexpr int kRaw = kTile * D * 4;
+  static constexpr int kRes = 2 * kTile * EST * 2;  // hi and lo rows
+  static constexpr int kBytes = kRaw > kRes ? kRaw : kRes;
 };
 
+__device__ __forceinline__ void split_f16(double x, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(static_cast<float>(x));
+  lo = static_cast<_Float16>(static_cast<float>(x - static_cast<double>(hi)));
+}
+
 template <int D, int BM, bool QJL>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 2)
 encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restrict__ K,
               uint8_t* __restrict__ codes) {
   constexpr int N = D / 2;
@@ -49,16 +65,19 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
   constexpr int M = QJL ? D : 0;
   constexpr int NSW = M / 32;
   constexpr int NW = NC + NSW;
-  constexpr int CPT = D / 4;            // channels per lane in the transform phase
-  constexpr int RPT = QJL ? M / 4 : 1;  // sketch rows per lane in the projection
+  constexpr int CPT = D / 4;          // channels per lane in the transform phase
   constexpr int EST = EncodeSmem<D>::EST;
+  constexpr int KSTEPS = D / 16;      // MFMA contraction steps
+  // D = 128: wave w owns sketch rows [32w, 32w+32) for both 32-key halves.
+  // D = 64:  wave w owns rows [32 (w&1), +32) for keys [32 (w>>1), +32).
+  constexpr int MT_PER_WAVE = D == 128 ? 2 : 1;
   static_assert(N % 32 == 0, "pairs must fill whole words");
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int h = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int64_t t0 = int64_t(blockIdx.x) * kTile;
-  const int nvalid = static_cast<int>(min<int64_t>(kTile, a.n_tokens - t0));
   const int esize = a.k_dtype == DT_F32 ? 4 : 2;
 
   __shared__ double s_T2[L];
@@ -66,7 +85,7 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
   __shared__ double s_LS[L * A];
   __shared__ int s_perm[D];
   __shared__ double s_sign[D];
-  __shared__ __align__(16) unsigned char s_raw[EncodeSmem<D>::kRawBytes];
+  __shared__ __align__(16) unsigned char s_raw[EncodeSmem<D>::kBytes];
   __shared__ uint8_t s_code[kTile][N + 4];
   __shared__ uint32_t s_sw[kTile][NSW > 0 ? NSW : 1];
   __shared__ uint16_t s_nu[kTile];
@@ -76,7 +95,7 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
   const double tscale = a.hadamard ? double(D) : 1.0;  // X = sqrt(d) k~ under the transform
   for (int i = tid; i < L; i += kThreads) {
     if (i < L - 1) {
-      double t = double(cb[L + i]);
+      const double t = double(cb[L + i]);
       s_T2[i] = tscale * t * t;  // exact: 24-bit significand squared, power-of-two factor
     } else {
       s_T2[i] = __longlong_as_double(0x7FF0000000000000ll);
@@ -95,167 +114,210 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
     s_sign[c] = double(a.signs[size_t(h) * D + c]);
   }
 
-  // ---- key tile -> LDS (16-byte coalesced loads; rows past n_tokens are zero)
-  {
-    const size_t row_bytes = size_t(D) * esize;
-    const uint8_t* src = K + ((size_t(b) * a.n_kv + h) * a.n_tokens + t0) * row_bytes;
-    const int tile_bytes = kTile * D * esize;
-    const int valid_bytes = nvalid * D * esize;
-    for (int off = tid * 16; off < tile_bytes; off += kThreads * 16) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (off < valid_bytes) v = *reinterpret_cast<const uint4*>(src + off);
-      *reinterpret_cast<uint4*>(s_raw + off) = v;
+  // ---- S_h as MFMA B operands (hi and lo), kept in registers for every tile:
+  //      lane holds S[row][16 ks + 8 (lane/32) + j], row = 32 nt + lane % 32
+  const int nt = D == 128 ? wave : (wave & 1);
+  const int mt0 = D == 128 ? 0 : (wave >> 1);
+  half8 sbh[QJL ? KSTEPS : 1], sbl[QJL ? KSTEPS : 1];
+  if constexpr (QJL) {
+    const float* srow = S + (size_t(h) * M + 32 * nt + (lane & 31)) * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const float4 u0 = *reinterpret_cast<const float4*>(srow + 16 * ks);
+      const float4 u1 = *reinterpret_cast<const float4*>(srow + 16 * ks + 4);
+      const float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        _Float16 hi, lo;
+        split_f16(double(v[j]), hi, lo);
+        sbh[ks][j] = hi;
+        sbl[ks][j] = lo;
+      }
     }
   }
+
+  double T2r[L - 1];
+  const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
+  const int64_t tile0 = int64_t(blockIdx.x) * kTilesPerBlock;
+  const int64_t tile1 = min<int64_t>(tile0 + kTilesPerBlock, n_tiles);
+  const double inv_scale = a.hadamard ? 1.0 / sqrt(double(D)) : 1.0;
+  uint8_t* base = codes + (size_t(b) * a.n_kv + h) * a.stream_bytes;
+  uint32_t* rows = reinterpret_cast<uint32_t*>(base);
+  const uint8_t* kstream = K + (size_t(b) * a.n_kv + h) * a.n_tokens * size_t(D) * esize;
   __syncthreads();
-
-  // ---- transform phase: key j on lanes 4j..4j+3, lane quarter qt holds channels
-  //      [qt*CPT, qt*CPT + CPT) of the reordered key
-  const int j = tid >> 2;
-  const int qt = tid & 3;
-  double x[CPT];
 #pragma unroll
-  for (int r = 0; r < CPT; ++r) {
-    const int c = qt * CPT + r;
-    const int src = s_perm[c];
-    double v;
-    if (esize == 4) {
-      v = double(reinterpret_cast<const float*>(s_raw)[j * D + src]);
-    } else {
-      v = double(__half2float(reinterpret_cast<const __half*>(s_raw)[j * D + src]));
+  for (int i = 0; i < L - 1; ++i) T2r[i] = s_T2[i];
+
+  for (int64_t tile = tile0; tile < tile1; ++tile) {
+    const int64_t t0 = tile * kTile;
+    const int nvalid = static_cast<int>(min<int64_t>(kTile, a.n_tokens - t0));
+
+    // ---- key tile -> LDS (16-byte coalesced loads; rows past n_tokens are zero)
+    {
+      const uint8_t* src = kstream + t0 * size_t(D) * esize;
+      const int tile_bytes = kTile * D * esize;
+      const int valid_bytes = nvalid * D * esize;
+      for (int off = tid * 16; off < tile_bytes; off += kThreads * 16) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (off < valid_bytes) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
+        *reinterpret_cast<u32x4*>(s_raw + off) = v;
+      }
     }
-    x[r] = a.hadamard ? v * s_sign[c] : v;
-  }
-  __syncthreads();  // the raw tile region is reused for the residual below
+    __syncthreads();
 
-  if (a.hadamard) {
+    // ---- transform phase: key j on lanes 4j..4j+3, quarter qt holds channels
+    //      [qt*CPT, qt*CPT + CPT) of the reordered key
+    const int j = tid >> 2;
+    const int qt = tid & 3;
+    double x[CPT];
 #pragma unroll
-    for (int hh = 1; hh < CPT; hh <<= 1) {
+    for (int r = 0; r < CPT; ++r) {
+      const int c = qt * CPT + r;
+      const int src = s_perm[c];
+      double v;
+      if (esize == 4) {
+        v = double(reinterpret_cast<const float*>(s_raw)[j * D + src]);
+      } else {
+        v = double(__half2float(reinterpret_cast<const __half*>(s_raw)[j * D + src]));
+      }
+      x[r] = a.hadamard ? v * s_sign[c] : v;
+    }
+    __syncthreads();  // the raw tile region is reused for the residual below
+
+    if (a.hadamard) {
+#pragma unroll
+      for (int hh = 1; hh < CPT; hh <<= 1) {
+#pragma unroll
+        for (int r = 0; r < CPT; ++r) {
+          if ((r & hh) == 0) {
+            const double u = x[r], w = x[r + hh];
+            x[r] = u + w;
+            x[r + hh] = u - w;
+          }
+        }
+      }
 #pragma unroll
       for (int r = 0; r < CPT; ++r) {
-        if ((r & hh) == 0) {
-          const double u = x[r], w = x[r + hh];
-          x[r] = u + w;
-          x[r + hh] = u - w;
+        const double p = quad_xor<1>(x[r]);
+        x[r] = (qt & 1) ? (p - x[r]) : (x[r] + p);
+      }
+#pragma unroll
+      for (int r = 0; r < CPT; ++r) {
+        const double p = quad_xor<2>(x[r]);
+        x[r] = (qt & 2) ? (p - x[r]) : (x[r] + p);
+      }
+    }
+
+    // ---- polar codes, residual
+    double ss = 0.0, mx = 0.0;
+#pragma unroll
+    for (int p = 0; p < CPT / 2; ++p) {
+      const double xx = x[2 * p], yy = x[2 * p + 1];
+      const double r2 = xx * xx + yy * yy;
+      int rc = 0;
+#pragma unroll
+      for (int i = 0; i < L - 1; ++i) rc += (T2r[i] < r2) ? 1 : 0;
+      const int ac = octant_cell(xx, yy) >> (3 - BA);
+      s_code[j][qt * (CPT / 2) + p] = static_cast<uint8_t>(rc | (ac << BM));
+      if constexpr (QJL) {
+        const double ex = xx * inv_scale - s_LC[rc * A + ac];
+        const double ey = yy * inv_scale - s_LS[rc * A + ac];
+        x[2 * p] = ex;
+        x[2 * p + 1] = ey;
+        ss += ex * ex + ey * ey;
+        mx = fmax(mx, fmax(fabs(ex), fabs(ey)));
+      }
+    }
+
+    if constexpr (QJL) {
+      const double s1 = ss + quad_xor<1>(ss);
+      const double s2 = s1 + quad_xor<2>(s1);
+      if (qt == 0) s_nu[j] = f64_to_f16_rne_sat(sqrt(s2));
+      // power-of-two scale that brings the largest residual entry of the key
+      // to [1, 2): exact, and no sign changes
+      double m1 = fmax(mx, quad_xor<1>(mx));
+      m1 = fmax(m1, quad_xor<2>(m1));
+      const double scl = m1 > 0.0 ? ldexp(1.0, -ilogb(m1)) : 1.0;
+      _Float16* Ehi = reinterpret_cast<_Float16*>(s_raw);
+      _Float16* Elo = Ehi + kTile * EST;
+#pragma unroll
+      for (int r = 0; r < CPT; ++r) {
+        _Float16 hi, lo;
+        split_f16(x[r] * scl, hi, lo);
+        Ehi[j * EST + qt * CPT + r] = hi;
+        Elo[j * EST + qt * CPT + r] = lo;
+      }
+    }
+    __syncthreads();
+
+    // ---- QJL projection on the matrix cores; sign words from ballots
+    if constexpr (QJL) {
+      const _Float16* Ehi = reinterpret_cast<const _Float16*>(s_raw);
+      const _Float16* Elo = Ehi + kTile * EST;
+#pragma unroll
+      for (int mi = 0; mi < MT_PER_WAVE; ++mi) {
+        const int mt = mt0 + mi;
+        const int key = 32 * mt + (lane & 31);
+        f32x16 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const int off = key * EST + 16 * ks + 8 * (lane >> 5);
+          const half8 ah = *reinterpret_cast<const half8*>(Ehi + off);
+          const half8 al = *reinterpret_cast<const half8*>(Elo + off);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, sbh[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, sbl[ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, sbh[ks], acc, 0, 0, 0);
+        }
+        // accumulator element r of lane l: key 8 (r/4) + 4 (l/32) + r%4 of the
+        // 32-key half, sketch row 32 nt + l%32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint64_t bal = __ballot(acc[r] >= 0.0f);
+          if (lane == 0) {
+            const int ka = 32 * mt + 8 * (r >> 2) + (r & 3);
+            s_sw[ka][nt] = static_cast<uint32_t>(bal);
+            s_sw[ka + 4][nt] = static_cast<uint32_t>(bal >> 32);
+          }
         }
       }
     }
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const double p = quad_xor<1>(x[r]);
-      x[r] = (qt & 1) ? (p - x[r]) : (x[r] + p);
-    }
-#pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const double p = quad_xor<2>(x[r]);
-      x[r] = (qt & 2) ? (p - x[r]) : (x[r] + p);
-    }
-  }
+    __syncthreads();
 
-  // ---- polar codes, residual
-  double T2r[L - 1];
+    // ---- pack and store: word w of token lane goes to row w, slot token_offset + t0 + lane
+    const int64_t slot = a.token_offset + t0 + lane;
+    const bool live = lane < nvalid;
 #pragma unroll
-  for (int i = 0; i < L - 1; ++i) T2r[i] = s_T2[i];
-  const double inv_scale = a.hadamard ? 1.0 / sqrt(double(D)) : 1.0;
-  double ss = 0.0;
+    for (int w = 0; w < NC; ++w) {
+      if ((w & 3) == wave) {
+        uint32_t word = 0;
 #pragma unroll
-  for (int p = 0; p < CPT / 2; ++p) {
-    const double xx = x[2 * p], yy = x[2 * p + 1];
-    const double r2 = xx * xx + yy * yy;
-    int rc = 0;
-#pragma unroll
-    for (int i = 0; i < L - 1; ++i) rc += (T2r[i] < r2) ? 1 : 0;
-    const int ac = octant_cell(xx, yy) >> (3 - BA);
-    s_code[j][qt * (CPT / 2) + p] = static_cast<uint8_t>(rc | (ac << BM));
+        for (int i = (32 * w) / P; i <= (32 * w + 31) / P && i < N; ++i) {
+          const uint32_t code = s_code[lane][i];
+          const int o = P * i - 32 * w;
+          word |= o >= 0 ? (code << o) : (code >> (-o));
+        }
+        if (live) rows[size_t(w) * a.capacity + slot] = word;
+      }
+    }
     if constexpr (QJL) {
-      const double ex = xx * inv_scale - s_LC[rc * A + ac];
-      const double ey = yy * inv_scale - s_LS[rc * A + ac];
-      x[2 * p] = ex;
-      x[2 * p + 1] = ey;
-      ss += ex * ex + ey * ey;
-    }
-  }
-
-  if constexpr (QJL) {
-    double s1 = ss + quad_xor<1>(ss);
-    double s2 = s1 + quad_xor<2>(s1);
-    if (qt == 0) s_nu[j] = f64_to_f16_rne_sat(sqrt(s2));
-    float* E = reinterpret_cast<float*>(s_raw);
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) E[j * EST + qt * CPT + r] = static_cast<float>(x[r]);
-  }
-  __syncthreads();
-
-  // ---- QJL projection: lane = key, wavefront = quarter of the sketch rows
-  if constexpr (QJL) {
-    const int jk = tid & 63;
-    const int rq = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const float* E = reinterpret_cast<const float*>(s_raw) + jk * EST;
-    const float* Sr = S + (size_t(h) * M + size_t(rq) * RPT) * D;
-    float acc[RPT];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) acc[r] = 0.0f;
-#pragma unroll 2
-    for (int c = 0; c < D; c += 4) {
-      const float4 e = *reinterpret_cast<const float4*>(E + c);
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const float4 s4 = *reinterpret_cast<const float4*>(Sr + size_t(r) * D + c);
-        float t = acc[r];
-        t = fmaf(s4.x, e.x, t);
-        t = fmaf(s4.y, e.y, t);
-        t = fmaf(s4.z, e.z, t);
-        t = fmaf(s4.w, e.w, t);
-        acc[r] = t;
+      for (int w = 0; w < NSW; ++w) {
+        if (((NC + w) & 3) == wave && live) rows[size_t(NC + w) * a.capacity + slot] = s_sw[lane][w];
+      }
+      if (((NC + NSW) & 3) == wave && live) {
+        uint16_t* nu = reinterpret_cast<uint16_t*>(base + size_t(4) * NW * a.capacity);
+        nu[slot] = s_nu[lane];
       }
     }
-    uint32_t bits = 0;
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) bits |= (acc[r] >= 0.0f ? 1u : 0u) << r;
-    if (RPT == 32) {
-      s_sw[jk][rq] = bits;
-    } else {
-      reinterpret_cast<uint16_t*>(&s_sw[jk][0])[rq] = static_cast<uint16_t>(bits);
-    }
-  }
-  __syncthreads();
-
-  // ---- pack and store: word w of token j goes to row w, slot token_offset + t0 + j
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  uint8_t* base = codes + (size_t(b) * a.n_kv + h) * a.stream_bytes;
-  uint32_t* rows = reinterpret_cast<uint32_t*>(base);
-  const int64_t slot = a.token_offset + t0 + lane;
-  const bool live = lane < nvalid;
-#pragma unroll
-  for (int w = 0; w < NC; ++w) {
-    if ((w & 3) == wave) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int i = (32 * w) / P; i <= (32 * w + 31) / P && i < N; ++i) {
-        const uint32_t code = s_code[lane][i];
-        const int o = P * i - 32 * w;
-        word |= o >= 0 ? (code << o) : (code >> (-o));
-      }
-      if (live) rows[size_t(w) * a.capacity + slot] = word;
-    }
-  }
-  if constexpr (QJL) {
-#pragma unroll
-    for (int w = 0; w < NSW; ++w) {
-      if (((NC + w) & 3) == wave && live) rows[size_t(NC + w) * a.capacity + slot] = s_sw[lane][w];
-    }
-    if (((NC + NSW) & 3) == wave && live) {
-      uint16_t* nu = reinterpret_cast<uint16_t*>(base + size_t(4) * NW * a.capacity);
-      nu[slot] = s_nu[lane];
-    }
+    __syncthreads();  // LDS is reused by the next tile
   }
 }
 
 template <int D, int BM, bool QJL>
 hipError_t launch_encode_t(const EncodeArgs& a, hipStream_t s) {
-  dim3 grid(static_cast<unsigned>((a.n_tokens + kTile - 1) / kTile), static_cast<unsigned>(a.n_kv),
-            static_cast<unsigned>(a.n_seq));
+  const int64_t n_tiles = (a.n_tokens + kTile - 1) / kTile;
+  dim3 grid(static_cast<unsigned>((n_tiles + kTilesPerBlock - 1) / kTilesPerBlock),
+            static_cast<unsigned>(a.n_kv), static_cast<unsigned>(a.n_seq));
   hipLaunchKernelGGL((encode_kernel<D, BM, QJL>), grid, dim3(kThreads), 0, s, a, a.S,
                      static_cast<const uint8_t*>(a.K), a.codes);
   return hipGetLastError();

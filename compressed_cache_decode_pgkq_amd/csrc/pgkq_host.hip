@@ -17,6 +17,7 @@ namespace {
 using pgkq::Geometry;
 
 constexpr int64_t kMaxGridYZ = 65535;
+constexpr int64_t kCalibRows = 2048;  // token rows per calibration workgroup
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -249,8 +250,7 @@ size_t pgkq_calibrate_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64
                                       int64_t n_tokens) {
   Geometry g;
   if (check_params(p, &g) != PGKQ_OK || n_seq < 1 || n_kv < 1 || n_tokens < 1) return 0;
-  const int64_t rows = n_seq * n_tokens;
-  const int64_t chunks = (rows + 4095) / 4096;
+  const int64_t chunks = n_seq * ((n_tokens + kCalibRows - 1) / kCalibRows);
   return round_up(size_t(n_kv) * chunks * g.d * sizeof(double), 256);
 }
 
@@ -278,9 +278,10 @@ pgkq_status pgkq_calibrate(const pgkq_params* p, const void* K, pgkq_dtype k_dty
   a.n_seq = n_seq;
   a.n_kv = n_kv;
   a.n_tokens = n_tokens;
-  a.rows_per_chunk = 4096;
-  a.n_chunks = (n_seq * n_tokens + 4095) / 4096;
-  if (a.n_chunks > 0x7FFFFFFF) return PGKQ_ERR_SHAPE;
+  a.rows_per_chunk = kCalibRows;
+  a.chunks_per_seq = (n_tokens + kCalibRows - 1) / kCalibRows;
+  a.n_chunks = n_seq * a.chunks_per_seq;
+  if (a.chunks_per_seq > 0x7FFFFFFF) return PGKQ_ERR_SHAPE;
   a.partial = static_cast<double*>(workspace);
   a.sumsq = sumsq;
   a.perm = perm;

@@ -43,7 +43,8 @@ struct CalibArgs {
   int d;
   int64_t n_seq, n_kv, n_tokens;
   int64_t rows_per_chunk;
-  int64_t n_chunks;
+  int64_t chunks_per_seq;  // token chunks per (sequence, kv-head) stream
+  int64_t n_chunks;        // chunks per kv-head = n_seq * chunks_per_seq
   double* partial;  // [n_kv][n_chunks][d]
   double* sumsq;    // [n_kv][d]
   uint16_t* perm;   // [n_kv][d] or null
