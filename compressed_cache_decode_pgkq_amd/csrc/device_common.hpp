@@ -155,13 +155,33 @@ __device__ __forceinline__ float quad_xor_f(float v) {
 // are half-open [e_a, e_{a+1}) counter-clockwise, theta = pi counted as -pi
 // (cell 0), and the zero vector taken as theta = 0 (cell 4).  Coarser grids
 // are prefixes: cell_b = cell_3 >> (3 - b).
+// Written branch-free on the comparison bits.
 __device__ __forceinline__ int octant_cell(double x, double y) {
-  if (x == 0.0 && y == 0.0) return 4;
-  const bool hi = (y > 0.0) || (y == 0.0 && x > 0.0);
-  const bool quarter = hi ? (x <= 0.0) : (x >= 0.0);
+  const int ypos = y > 0.0, yzero = y == 0.0, xneg = x < 0.0, xzero = x == 0.0;
+  const int hi = ypos | (yzero & (xneg ^ 1));             // theta in [0, pi)
+  const int q_hi = (xneg | xzero) & ypos;                  // [pi/2, pi)
+  const int q_lo = xneg ^ 1;                               // [-pi/2, 0)
+  const int quarter = hi ? q_hi : q_lo;
   const double ax = fabs(x), ay = fabs(y);
-  const bool sub = quarter ? (ay <= ax) : (ay >= ax);
-  return (hi ? 4 : 0) + (quarter ? 2 : 0) + (sub ? 1 : 0);
+  const int le = ay <= ax, ge = ay >= ax;
+  const int sub = (quarter ? le : ge) & ((xzero & yzero) ^ 1);  // zero vector: theta = 0
+  return (hi << 2) | (quarter << 1) | sub;
+}
+
+// fp64 -> fp16 bits (nearest, ties to even; beyond range saturates to 65504)
+// for non-negative x: round to fp32 with round-to-odd (truncate, then set the
+// last bit if anything was dropped), then round that to fp16.  With 13 spare
+// bits in the fp32 significand the second rounding equals a single direct
+// rounding of x.
+__device__ __forceinline__ uint16_t f64_to_f16_rne_sat_nonneg(double x) {
+  float f = static_cast<float>(x);                       // nearest
+  uint32_t u = __float_as_uint(f);
+  const double back = static_cast<double>(f);
+  u -= (back > x) ? 1u : 0u;                             // now truncated toward zero
+  u |= (static_cast<double>(__uint_as_float(u)) != x) ? 1u : 0u;  // sticky bit
+  f = __uint_as_float(u);
+  f = fminf(f, 65504.0f);                                // saturate (65504 is exact)
+  return __half_as_ushort(__float2half_rn(f));
 }
 
 }  // namespace pgkq
