@@ -225,9 +225,23 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   }
   __syncthreads();
 
-  for (int64_t c0 = t_begin + int64_t(wave) * kWave; c0 < t_end; c0 += kScanThreads) {
+  // Token ranges: either the workgroup's split is shared by its wavefronts in
+  // interleaved chunks, or (wave_parts) every wavefront scans a contiguous
+  // partition of its own and writes its own partial state.
+  int64_t c_first, c_end, c_step;
+  if (a.wave_parts) {
+    const int64_t tpw = a.tokens_per_split / kScanWaves;
+    c_first = t_begin + int64_t(wave) * tpw;
+    c_end = min<int64_t>(c_first + tpw, t_end);
+    c_step = kWave;
+  } else {
+    c_first = t_begin + int64_t(wave) * kWave;
+    c_end = t_end;
+    c_step = kScanThreads;
+  }
+  for (int64_t c0 = c_first; c0 < c_end; c0 += c_step) {
     const int64_t t = c0 + lane;
-    const bool valid = t < t_end;
+    const bool valid = t < c_end;
     load_codes(c0);
     if constexpr (!LOGITS) sm.load_v(vc, c0, vrs);
 
@@ -290,8 +304,13 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     }
   }
   if constexpr (!LOGITS) {
-    __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
-    sm.finish(s_tab, tid, a.n_splits, split, a.out, a.partial, size_t(b) * a.n_q + size_t(h) * G);
+    const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
+    if (a.wave_parts) {
+      sm.finish_wave(a.partial, row0, split * kScanWaves + wave, a.n_splits * kScanWaves);
+    } else {
+      __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
+      sm.finish(s_tab, tid, a.n_splits, split, a.out, a.partial, row0);
+    }
   }
 }
 

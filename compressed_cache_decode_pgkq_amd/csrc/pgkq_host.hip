@@ -58,27 +58,51 @@ pgkq_status map_hip(hipError_t e) { return e == hipSuccess ? PGKQ_OK : PGKQ_ERR_
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Splits {
-  int n;
-  int64_t tokens_per;
+  int n;             // workgroups per (sequence, kv-head)
+  int64_t tokens_per;  // tokens per workgroup
+  int wave_parts;    // 1: one partition per wavefront (4 per workgroup)
+  int partials() const { return wave_parts ? 4 * n : n; }
 };
 
-// Token splits per (sequence, kv-head): enough workgroups to cover the chip
-// (about 2048 in flight) without splits shorter than one wavefront chunk.
-Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested) {
+constexpr int kScanWaves = 4;
+
+// Partitions of the token axis per (sequence, kv-head).  Automatic: about
+// 2048 wavefronts of work in flight.  With many streams, workgroup splits of at
+// least 512 tokens whose wavefronts interleave 64-token chunks; with few long
+// streams (fewer than 64), one partition per wavefront, about 2048 in total.
+// A requested count is honoured as the number of partial states merged per
+// query head; when its partitions are short (at most 1024 tokens) each
+// workgroup runs four consecutive partitions, one per wavefront, sharing one
+// build of the lookup tables.
+Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested,
+                     bool allow_wave_parts = true) {
+  if (requested == 0 && allow_wave_parts && n_units < 64) {
+    requested = static_cast<int32_t>(
+        std::min<int64_t>((2048 + n_units - 1) / n_units, std::max<int64_t>(1, n_tokens / 256)));
+  }
+  if (allow_wave_parts && requested >= 2 * kScanWaves) {
+    int64_t tpw = (n_tokens + requested - 1) / requested;
+    tpw = std::max<int64_t>(64, round_up(static_cast<size_t>(tpw), 64));
+    if (tpw <= 1024) {
+      const int64_t tps = kScanWaves * tpw;
+      const int64_t ns = std::max<int64_t>(1, (n_tokens + tps - 1) / tps);
+      return Splits{static_cast<int>(ns), tps, 1};
+    }
+  }
   int64_t ns = requested > 0 ? requested : (2048 + n_units - 1) / n_units;
-  const int64_t min_tokens = requested > 0 ? 64 : 256;
+  const int64_t min_tokens = requested > 0 ? 64 : 512;
   const int64_t max_ns = std::max<int64_t>(1, (n_tokens + min_tokens - 1) / min_tokens);
   ns = std::min<int64_t>(std::max<int64_t>(ns, 1), max_ns);
   int64_t tps = (n_tokens + ns - 1) / ns;
   tps = std::max<int64_t>(64, round_up(static_cast<size_t>(tps), 64));
   ns = std::max<int64_t>(1, (n_tokens + tps - 1) / tps);
-  return Splits{static_cast<int>(ns), tps};
+  return Splits{static_cast<int>(ns), tps, 0};
 }
 
 size_t decode_ws(const Geometry& g, int64_t n_seq, int64_t n_q, const Splits& sp) {
   const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
   size_t bytes = round_up(size_t(n_seq) * n_q * pl.stride() * sizeof(float), 256);
-  if (sp.n > 1) bytes += round_up(size_t(n_seq) * n_q * sp.n * (g.d + 4) * sizeof(float), 256);
+  if (sp.partials() > 1) bytes += round_up(size_t(n_seq) * n_q * sp.partials() * (g.d + 4) * sizeof(float), 256);
   return bytes;
 }
 
@@ -394,8 +418,9 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   a.prep = static_cast<float*>(workspace);
   a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                        round_up(size_t(n_seq) * n_q * pl.stride() * 4, 256));
-  a.n_splits = logits_mode ? sp.n : sp.n;
+  a.n_splits = sp.n;
   a.tokens_per_split = sp.tokens_per;
+  a.wave_parts = sp.wave_parts;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(g.d));
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e = pgkq::launch_query_prep(g, a, s);
@@ -410,8 +435,8 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
     if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
       return PGKQ_ERR_HIP;
   }
-  if (!logits_mode && a.n_splits > 1) {
-    e = pgkq::launch_partial_merge(g.d, n_seq, n_q, a.n_splits, a.partial, out, s);
+  if (!logits_mode && sp.partials() > 1) {
+    e = pgkq::launch_partial_merge(g.d, n_seq, n_q, sp.partials(), a.partial, out, s);
     if (e != hipSuccess) return PGKQ_ERR_HIP;
   }
   return PGKQ_OK;
@@ -447,7 +472,7 @@ size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t
   if ((head_dim != 64 && head_dim != 128) || n_seq < 1 || n_q < 1 || n_kv < 1 || n_tokens < 0)
     return 0;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
-                                  opts ? opts->n_splits : 0);
+                                  opts ? opts->n_splits : 0, false);
   return fp16_ws(head_dim, n_seq, n_q, sp);
 }
 
@@ -468,7 +493,7 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
       (workspace && !aligned16(workspace)))
     return PGKQ_ERR_ALIGN;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
-                                  opts ? opts->n_splits : 0);
+                                  opts ? opts->n_splits : 0, false);
   const size_t need = fp16_ws(head_dim, n_seq, n_q, sp);
   if (need && (!workspace || workspace_bytes < need)) return PGKQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -80,9 +80,10 @@ struct DecodeArgs {
   float* out;           // final output (n_splits == 1) or null
   float* logits;        // logits mode output or null
   float* prep;          // workspace: query prep
-  float* partial;       // workspace: split partial states [n_seq][n_q][n_splits][d + 4]
-  int n_splits;
+  float* partial;       // workspace: partial states [n_seq][n_q][n_partials][d + 4]
+  int n_splits;         // workgroups per (sequence, kv-head)
   int64_t tokens_per_split;
+  int wave_parts;       // 1: each wavefront scans its own partition (n_partials = 4 n_splits)
   float scale_log2;     // softmax scale * log2(e)
 };
 

@@ -125,6 +125,33 @@ struct SoftmaxPV {
     wave_lds_sync();
   }
 
+  // Write this wavefront's own state as partial `pidx` of `n_parts` for the
+  // query heads row0 .. row0 + G - 1 (no LDS, no barrier): used when every
+  // wavefront scans a partition of its own.
+  __device__ __forceinline__ void finish_wave(float* __restrict__ partial, size_t row0, int pidx,
+                                              int n_parts) {
+#pragma unroll
+    for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[g][k] += __shfl_xor(o[g][k], off, kWave);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float l_w = wave_sum(l_lane[g]);
+      float* part = partial + ((row0 + g) * n_parts + pidx) * (D + 4);
+      if (lane < LPT) {
+        *reinterpret_cast<float4*>(part + 4 + dblk * 8) = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+        *reinterpret_cast<float4*>(part + 8 + dblk * 8) = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+      }
+      if (lane == 0) {
+        part[0] = m_run[g];
+        part[1] = l_w;
+      }
+    }
+  }
+
   // Merge the wavefronts through `scratch` (MERGE_FLOATS floats of LDS, free to
   // reuse: the caller synchronizes before) and write the state of query heads
   // hq0 .. hq0 + G - 1.  out: [.., D] rows at out_row(g); partial rows likewise.

@@ -159,7 +159,7 @@ def _check_decode(case, n_splits=0, q_override=None, q_dtype=None):
 
 
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("n_splits", [1, 0, 7])
+@pytest.mark.parametrize("n_splits", [1, 0, 7, 12, 256])  # 12, 256: one partition per wavefront
 def test_decode_matches_oracle_on_identical_codes(name, n_splits):
     cfg, kw = SMALL[name]
     _check_decode(Case(cfg, **kw), n_splits=n_splits)
@@ -183,6 +183,7 @@ def test_decode_ragged_lengths(T):
     case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=1000), n_tokens=T, capacity=1024)
     _check_decode(case, n_splits=0)
     _check_decode(case, n_splits=3)
+    _check_decode(case, n_splits=9)
 
 
 def test_decode_empty_cache_gives_zeros():
@@ -195,6 +196,19 @@ def test_decode_empty_cache_gives_zeros():
                          dev["V"], dev["signs"], None, dev["codebook"], dev["S"], n_tokens=0, out=out)
     torch.cuda.synchronize()
     assert torch.all(out == 0)
+
+
+@pytest.mark.parametrize("hadamard", [True, False])
+@pytest.mark.parametrize("qjl", [True, False])
+def test_ablation_grid_hadamard_by_qjl(hadamard, qjl):
+    """The 2x2 of the ablation paragraph (Hadamard on/off x QJL on/off, b_main = 3):
+    every cell encodes bit-exactly and decodes within the bars."""
+    cfg = CONFIGS["c2a"].with_(n_seq=2, qjl_m=64 if qjl else 0)
+    case = Case(cfg, hadamard=hadamard)
+    counts = _code_counts(case, _gpu_encode(case))
+    print(hadamard, qjl, counts)
+    assert_code_parity(counts)
+    _check_decode(case)
 
 
 def test_decode_without_hadamard():
