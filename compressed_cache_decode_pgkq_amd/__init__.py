@@ -18,6 +18,11 @@ from .api import (  # noqa: F401
     pgkq_fp16_decode_attn,
     pgkq_lloyd_max_beta,
     pgkq_record_bytes,
+    pgkq_rtn_decode_attn,
+    pgkq_rtn_decode_workspace_bytes,
+    pgkq_rtn_encode,
+    pgkq_rtn_logits,
+    pgkq_rtn_record_bytes,
     pgkq_version,
 )
 from ._lib import PgkqError  # noqa: F401

@@ -187,3 +187,64 @@ def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor,
                                        _stream(stream))
     L.check(st, "pgkq_fp16_decode_attn")
     return out
+
+
+# ---------------------------------------------------------------- RTN control
+
+
+def pgkq_rtn_record_bytes(head_dim: int, bits: int) -> int:
+    return int(L.lib().pgkq_rtn_record_bytes(head_dim, bits))
+
+
+def pgkq_rtn_encode(K: torch.Tensor, bits: int, codes=None, capacity=None, token_offset: int = 0,
+                    stream=None):
+    """K [n_seq, n_kv, n_tokens, d] (fp32 / fp16) -> codes [n_seq, n_kv, capacity * record] uint8."""
+    n_seq, n_kv, n_tok, d = K.shape
+    cap = int(capacity) if capacity is not None else n_tok
+    if codes is None:
+        rb = pgkq_rtn_record_bytes(d, bits)
+        codes = torch.zeros((n_seq, n_kv, cap * rb), dtype=torch.uint8, device=K.device)
+    st = L.lib().pgkq_rtn_encode(d, bits, _ptr(K), _dtype(K), n_seq, n_kv, n_tok, _ptr(codes), cap,
+                                 int(token_offset), _stream(stream))
+    L.check(st, "pgkq_rtn_encode")
+    return codes
+
+
+def pgkq_rtn_decode_workspace_bytes(head_dim, n_seq, n_q, n_kv, n_tokens, n_splits=0) -> int:
+    o = _opts(n_splits, None)
+    return int(L.lib().pgkq_rtn_decode_workspace_bytes(head_dim, n_seq, n_q, n_kv, n_tokens,
+                                                        ctypes.byref(o)))
+
+
+def pgkq_rtn_decode_attn(q: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, bits: int,
+                         n_tokens=None, softmax_scale: float = 0.0, n_splits: int = 0, out=None,
+                         workspace=None, events=None, stream=None):
+    """q [n_seq, n_q, d]; codes [n_seq, n_kv, cap * record]; V [n_seq, n_kv, cap, d] fp16."""
+    n_seq, n_q, d = q.shape
+    n_kv, cap = V.shape[1], V.shape[2]
+    n_tok = cap if n_tokens is None else int(n_tokens)
+    o = _opts(n_splits, events)
+    if out is None:
+        out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    nb = int(L.lib().pgkq_rtn_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, ctypes.byref(o)))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_rtn_decode_attn(d, bits, _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap,
+                                      _ptr(codes), _ptr(V), _ptr(out), float(softmax_scale),
+                                      ctypes.byref(o), _ptr(ws), wsb, _stream(stream))
+    L.check(st, "pgkq_rtn_decode_attn")
+    return out
+
+
+def pgkq_rtn_logits(q: torch.Tensor, codes: torch.Tensor, n_kv: int, capacity: int, bits: int,
+                    n_tokens=None, logits=None, workspace=None, stream=None):
+    """Raw RTN logits [n_seq, n_q, n_tokens] fp32."""
+    n_seq, n_q, d = q.shape
+    n_tok = capacity if n_tokens is None else int(n_tokens)
+    if logits is None:
+        logits = torch.empty((n_seq, n_q, n_tok), dtype=torch.float32, device=q.device)
+    nb = int(L.lib().pgkq_rtn_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, None))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_rtn_logits(d, bits, _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, capacity,
+                                 _ptr(codes), _ptr(logits), _ptr(ws), wsb, _stream(stream))
+    L.check(st, "pgkq_rtn_logits")
+    return logits

@@ -57,6 +57,14 @@ pgkq_status map_hip(hipError_t e) { return e == hipSuccess ? PGKQ_OK : PGKQ_ERR_
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// The scans address one stream's codes and value rows through buffer
+// resources with 32-bit byte ranges and offsets.
+constexpr size_t kMaxStreamBytes = 0xFFFFFFF0u;
+bool fits_buffer(int64_t capacity, size_t record_bytes, int d) {
+  return size_t(capacity) * record_bytes <= kMaxStreamBytes &&
+         size_t(capacity) * size_t(d) * 2 <= kMaxStreamBytes;
+}
+
 struct Splits {
   int n;             // workgroups per (sequence, kv-head)
   int64_t tokens_per;  // tokens per workgroup
@@ -122,6 +130,22 @@ hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
   const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096));
   hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, s, p, n);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RTN control
+
+pgkq_status check_rtn(int32_t head_dim, int32_t bits) {
+  if (head_dim != 64 && head_dim != 128) return PGKQ_ERR_UNSUPPORTED;
+  if (bits != 3 && bits != 4) return PGKQ_ERR_UNSUPPORTED;
+  return PGKQ_OK;
+}
+
+size_t rtn_record(int d, int bits) { return size_t(d) * bits / 8 + 4; }
+
+size_t rtn_ws(int d, int group, int64_t n_seq, int64_t n_q, int64_t n_kv, const Splits& sp) {
+  size_t bytes = round_up(size_t(n_seq) * n_kv * pgkq::rtn_prep_stride(d, group) * sizeof(float), 256);
+  if (sp.partials() > 1) bytes += round_up(size_t(n_seq) * n_q * sp.partials() * (d + 4) * sizeof(float), 256);
+  return bytes;
 }
 
 // ---------------------------------------------------------------- Lloyd-Max
@@ -383,6 +407,7 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
   if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
   if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;
+  if (!fits_buffer(capacity, g.record_bytes(), g.d)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
       !aligned16(workspace) || (perm && !aligned16(perm)) || (S && !aligned16(S)) ||
       (V && !aligned16(V)) || (out && !aligned16(out)) || (logits && !aligned16(logits)))
@@ -489,6 +514,7 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   int group = 0;
   if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
   if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (!fits_buffer(capacity, 0, head_dim)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(K16) || !aligned16(V16) || !aligned16(out) ||
       (workspace && !aligned16(workspace)))
     return PGKQ_ERR_ALIGN;
@@ -528,6 +554,142 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   }
   if (sp.n > 1) return map_hip(pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.n, a.partial, out, s));
   return PGKQ_OK;
+}
+
+size_t pgkq_rtn_record_bytes(int32_t head_dim, int32_t bits) {
+  if (check_rtn(head_dim, bits) != PGKQ_OK) return 0;
+  return rtn_record(head_dim, bits);
+}
+
+pgkq_status pgkq_rtn_encode(int32_t head_dim, int32_t bits, const void* K, pgkq_dtype k_dtype,
+                            int64_t n_seq, int64_t n_kv, int64_t n_tokens, void* codes,
+                            int64_t capacity, int64_t token_offset, void* stream) {
+  pgkq_status st = check_rtn(head_dim, bits);
+  if (st != PGKQ_OK) return st;
+  if (!K || !codes) return PGKQ_ERR_NULL;
+  if ((st = check_dtype(k_dtype, false)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  if (n_tokens < 0 || token_offset < 0 || capacity < 1) return PGKQ_ERR_SHAPE;
+  if (token_offset + n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if ((n_tokens + 255) / 256 > 0x7FFFFFFF) return PGKQ_ERR_SHAPE;
+  if (!aligned16(K) || !aligned16(codes)) return PGKQ_ERR_ALIGN;
+  if (n_tokens == 0) return PGKQ_OK;
+  pgkq::RtnEncodeArgs a{};
+  a.K = K;
+  a.k_dtype = static_cast<int>(k_dtype);
+  a.d = head_dim;
+  a.bits = bits;
+  a.n_seq = n_seq;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.token_offset = token_offset;
+  a.codes = static_cast<uint8_t*>(codes);
+  a.stream_bytes = size_t(capacity) * rtn_record(head_dim, bits);
+  return map_hip(pgkq::launch_rtn_encode(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pgkq_rtn_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q, int64_t n_kv,
+                                       int64_t n_tokens, const pgkq_launch_opts* opts) {
+  if ((head_dim != 64 && head_dim != 128) || n_seq < 1 || n_q < 1 || n_kv < 1 || n_tokens < 0)
+    return 0;
+  int group = 0;
+  if (check_group(n_q, n_kv, &group) != PGKQ_OK) return 0;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  return rtn_ws(head_dim, group, n_seq, n_q, n_kv, sp);
+}
+
+static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void* q,
+                                     pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q, int64_t n_kv,
+                                     int64_t n_tokens, int64_t capacity, const void* codes,
+                                     const void* V, float* out, float* logits, float softmax_scale,
+                                     const pgkq_launch_opts* opts, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  pgkq_status st = check_rtn(head_dim, bits);
+  if (st != PGKQ_OK) return st;
+  const bool logits_mode = logits != nullptr;
+  if (!q || !codes || !workspace) return PGKQ_ERR_NULL;
+  if (!logits_mode && (!V || !out)) return PGKQ_ERR_NULL;
+  if ((st = check_dtype(q_dtype, true)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  int group = 0;
+  if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
+  if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (!fits_buffer(capacity, rtn_record(head_dim, bits), head_dim)) return PGKQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(codes) || !aligned16(workspace) || (V && !aligned16(V)) ||
+      (out && !aligned16(out)) || (logits && !aligned16(logits)))
+    return PGKQ_ERR_ALIGN;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  if (workspace_bytes < rtn_ws(head_dim, group, n_seq, n_q, n_kv, sp)) return PGKQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tokens == 0) {
+    if (logits_mode) return PGKQ_OK;
+    return map_hip(zero_fill(out, size_t(n_seq) * n_q * head_dim, s));
+  }
+  pgkq::RtnDecodeArgs a{};
+  a.q = q;
+  a.q_dtype = static_cast<int>(q_dtype);
+  a.d = head_dim;
+  a.bits = bits;
+  a.n_seq = n_seq;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.group = group;
+  a.codes = static_cast<const uint8_t*>(codes);
+  a.stream_bytes = size_t(capacity) * rtn_record(head_dim, bits);
+  a.V = static_cast<const __half*>(V);
+  a.out = out;
+  a.logits = logits;
+  a.prep = static_cast<float*>(workspace);
+  a.partial = reinterpret_cast<float*>(
+      static_cast<char*>(workspace) +
+      round_up(size_t(n_seq) * n_kv * pgkq::rtn_prep_stride(head_dim, group) * 4, 256));
+  a.n_splits = sp.n;
+  a.tokens_per_split = sp.tokens_per;
+  a.wave_parts = sp.wave_parts;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = pgkq::launch_rtn_query_prep(a, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_start) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  e = pgkq::launch_rtn_scan(a, logits_mode, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_stop) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  if (!logits_mode && sp.partials() > 1) {
+    e = pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.partials(), a.partial, out, s);
+    if (e != hipSuccess) return PGKQ_ERR_HIP;
+  }
+  return PGKQ_OK;
+}
+
+pgkq_status pgkq_rtn_decode_attn(int32_t head_dim, int32_t bits, const void* q, pgkq_dtype q_dtype,
+                                 int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                 int64_t capacity, const void* codes, const void* V, float* out,
+                                 float softmax_scale, const pgkq_launch_opts* opts,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return PGKQ_ERR_NULL;
+  return rtn_decode_common(head_dim, bits, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, codes,
+                           V, out, nullptr, softmax_scale, opts, workspace, workspace_bytes, stream);
+}
+
+pgkq_status pgkq_rtn_logits(int32_t head_dim, int32_t bits, const void* q, pgkq_dtype q_dtype,
+                            int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                            int64_t capacity, const void* codes, float* logits, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (!logits) return PGKQ_ERR_NULL;
+  return rtn_decode_common(head_dim, bits, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, codes,
+                           nullptr, nullptr, logits, 0.f, nullptr, workspace, workspace_bytes,
+                           stream);
 }
 
 }  // extern "C"

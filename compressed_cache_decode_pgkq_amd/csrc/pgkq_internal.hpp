@@ -102,6 +102,39 @@ struct Fp16DecodeArgs {
   float scale_log2;
 };
 
+// Per-token asymmetric RTN key cache (the INT3 / INT4 control).
+struct RtnEncodeArgs {
+  const void* K;
+  int k_dtype;
+  int d, bits;
+  int64_t n_seq, n_kv, n_tokens, capacity, token_offset;
+  uint8_t* codes;
+  size_t stream_bytes;   // capacity * record bytes
+};
+
+// RTN query preparation per (sequence, kv-head), floats:
+//   [ q[c][g] for c < d, g < G | sum_c q[c][g] for g < G | pad to 4 ]
+__host__ __device__ inline int rtn_prep_stride(int d, int G) { return (d * G + G + 3) & ~3; }
+
+struct RtnDecodeArgs {
+  const void* q;
+  int q_dtype;
+  int d, bits;
+  int64_t n_seq, n_q, n_kv, n_tokens, capacity;
+  int group;
+  const uint8_t* codes;
+  size_t stream_bytes;
+  const __half* V;
+  float* out;
+  float* logits;
+  float* prep;          // workspace: [n_seq][n_kv][rtn_prep_stride]
+  float* partial;       // workspace: partial states
+  int n_splits;
+  int64_t tokens_per_split;
+  int wave_parts;
+  float scale_log2;
+};
+
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_encode(const Geometry& g, const EncodeArgs& a, hipStream_t s);
 hipError_t launch_query_prep(const Geometry& g, const DecodeArgs& a, hipStream_t s);
@@ -110,5 +143,8 @@ hipError_t launch_decode_scan(const Geometry& g, const DecodeArgs& a, bool logit
 hipError_t launch_partial_merge(int d, int64_t n_seq, int64_t n_q, int n_splits,
                                 const float* partial, float* out, hipStream_t s);
 hipError_t launch_fp16_decode(const Fp16DecodeArgs& a, hipStream_t s);
+hipError_t launch_rtn_encode(const RtnEncodeArgs& a, hipStream_t s);
+hipError_t launch_rtn_query_prep(const RtnDecodeArgs& a, hipStream_t s);
+hipError_t launch_rtn_scan(const RtnDecodeArgs& a, bool logits_mode, hipStream_t s);
 
 }  // namespace pgkq

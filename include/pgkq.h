@@ -26,6 +26,9 @@
  *    error the function returns a non-zero pgkq_status and enqueues nothing.
  *    A HIP launch error maps to PGKQ_ERR_HIP.  No C++ exception crosses this ABI.
  *  - Device pointers must be 16-byte aligned.
+ *  - One stream's codes and one stream's value rows (capacity * d * 2 bytes)
+ *    must each stay under 4 GiB (the scans use 32-bit buffer offsets);
+ *    larger capacities are rejected with PGKQ_ERR_SHAPE.
  *  - n_tokens == 0 is a valid no-op (outputs untouched, except that decode
  *    attention writes zeros to `out` because an empty softmax has no weights).
  *
@@ -187,6 +190,58 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
                                   int32_t head_dim, const void* K16, const void* V16, float* out,
                                   float softmax_scale, const pgkq_launch_opts* opts,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * RTN control: per-token asymmetric round-to-nearest keys (EdgeLLM-Nano paper
+ * page, "Comparison to simpler baselines": K quantized per token to INT3 or
+ * INT4 with an FP16 scale and zero-point per key vector, V in FP16).
+ *
+ * Per key vector k (d values): zp = fp16(min_c k_c), hi = fp16(max_c k_c)
+ * (a -0 extreme counts as +0), scale = fp16((hi - zp) / (2^bits - 1)) rounded
+ * once from float64 (a zero result gives scale 1), and
+ *   code_c = clamp(nearest_even((k_c - zp) / scale), 0, 2^bits - 1)
+ * decided in float64.  The logit of token t is sum_c q_c (zp_t + scale_t code_tc).
+ * Keys must be finite and within the fp16 range.
+ *
+ * Record of one token slot: d*bits/8 + 4 bytes (36 / 28 at d = 64, i.e. 4.50 /
+ * 3.50 bits per element): NC = d*bits/32 code words holding the codes as one
+ * bit stream (code c at bits [bits*c, bits*c + bits), LSB first; bit q in word
+ * q/32, bit q%32), then one word with the fp16 scale in its low half and the
+ * fp16 zero-point in its high half.  Word w of token t is stored at byte
+ * 4 (w capacity + t) of the stream; streams back to back in [n_seq][n_kv]
+ * order.  head_dim 64 or 128, bits 3 or 4.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of one RTN token slot, 0 if (head_dim, bits) is unsupported. */
+size_t pgkq_rtn_record_bytes(int32_t head_dim, int32_t bits);
+
+/* Quantize K [n_seq][n_kv][n_tokens][d] (F32 or F16) into slots
+ * [token_offset, token_offset + n_tokens) of every stream of `codes`
+ * (n_seq * n_kv streams of `capacity` slots); other slots are untouched. */
+pgkq_status pgkq_rtn_encode(int32_t head_dim, int32_t bits, const void* K, pgkq_dtype k_dtype,
+                            int64_t n_seq, int64_t n_kv, int64_t n_tokens, void* codes,
+                            int64_t capacity, int64_t token_offset, void* stream);
+
+/* Bytes of workspace pgkq_rtn_decode_attn / pgkq_rtn_logits need (0 if the
+ * shape is invalid). */
+size_t pgkq_rtn_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q,
+                                       int64_t n_kv, int64_t n_tokens,
+                                       const pgkq_launch_opts* opts);
+
+/* Decode attention over RTN keys and fp16 values; q, V, out, softmax_scale,
+ * opts and the split / merge scheme as for pgkq_decode_attn. */
+pgkq_status pgkq_rtn_decode_attn(int32_t head_dim, int32_t bits, const void* q, pgkq_dtype q_dtype,
+                                 int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                 int64_t capacity, const void* codes, const void* V, float* out,
+                                 float softmax_scale, const pgkq_launch_opts* opts,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Raw RTN logits <q, k-hat_t> into logits [n_seq][n_q][n_tokens] fp32 (same
+ * device code as the score step of pgkq_rtn_decode_attn). */
+pgkq_status pgkq_rtn_logits(int32_t head_dim, int32_t bits, const void* q, pgkq_dtype q_dtype,
+                            int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                            int64_t capacity, const void* codes, float* logits, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

@@ -19,7 +19,8 @@ layout      bit-plane packing of the codes (and unpacking)
 attn        analytic logits, softmax and FP16-V weighted sum, split/merge,
             the FP16-cache comparator and an explicit dequantizer
 accounting  byte and bits-per-element accounting of the compressed cache
-rtn         per-token asymmetric round-to-nearest key quantization (control)
+rtn         per-token asymmetric round-to-nearest key quantization (control):
+            quantizer, record layout and decode attention
 
 Parity pins live in ``tests/test_oracle_pins.py``.  Parity unpinned: the
 absolute codebook values and the code values for any given input (the pages

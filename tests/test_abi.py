@@ -196,3 +196,77 @@ def test_workspace_sizes_grow_with_splits():
     w1 = api.pgkq_decode_workspace_bytes(p, 1, 32, 8, 131072, n_splits=1)
     w256 = api.pgkq_decode_workspace_bytes(p, 1, 32, 8, 131072, n_splits=256)
     assert w256 - w1 >= 32 * 256 * (128 + 4) * 4 - 256
+
+
+def test_buffer_range_limit_is_rejected():
+    # one stream's value rows beyond 4 GiB (32-bit buffer offsets): capacity * 128 * 2
+    assert _decode(cap=1 << 24, n_tok=100) == L.PGKQ_ERR_SHAPE
+    o = L.PgkqLaunchOpts(0, None, None)
+    st = L.lib().pgkq_fp16_decode_attn(_vp(A), L.PGKQ_F32, 1, 4, 4, 10, 1 << 24, 128, _vp(A),
+                                       _vp(A), _vp(A), 0.0, ctypes.byref(o), _vp(A), 1 << 30, None)
+    assert st == L.PGKQ_ERR_SHAPE
+
+
+@pytest.mark.parametrize("d,bits,rb", [(64, 3, 28), (64, 4, 36), (128, 3, 52), (128, 4, 68)])
+def test_rtn_record_bytes(d, bits, rb):
+    assert api.pgkq_rtn_record_bytes(d, bits) == rb
+
+
+@pytest.mark.parametrize("d,bits", [(64, 2), (64, 8), (96, 4), (128, 5)])
+def test_rtn_unsupported_has_no_record(d, bits):
+    assert api.pgkq_rtn_record_bytes(d, bits) == 0
+
+
+def _rtn_encode(d=64, bits=3, K=A, kd=L.PGKQ_F16, n_seq=2, n_kv=3, n_tok=16, codes=A, cap=16, off=0):
+    return L.lib().pgkq_rtn_encode(d, bits, _vp(K) if K else None, kd, n_seq, n_kv, n_tok,
+                                   _vp(codes) if codes else None, cap, off, None)
+
+
+def test_rtn_encode_validation():
+    assert _rtn_encode(K=0) == L.PGKQ_ERR_NULL
+    assert _rtn_encode(codes=0) == L.PGKQ_ERR_NULL
+    assert _rtn_encode(bits=2) == L.PGKQ_ERR_UNSUPPORTED
+    assert _rtn_encode(d=96) == L.PGKQ_ERR_UNSUPPORTED
+    assert _rtn_encode(kd=L.PGKQ_BF16) == L.PGKQ_ERR_UNSUPPORTED
+    assert _rtn_encode(n_seq=0) == L.PGKQ_ERR_SHAPE
+    assert _rtn_encode(n_tok=17) == L.PGKQ_ERR_SHAPE
+    assert _rtn_encode(off=1) == L.PGKQ_ERR_SHAPE
+    assert _rtn_encode(cap=0, n_tok=0) == L.PGKQ_ERR_SHAPE
+    assert _rtn_encode(K=MIS) == L.PGKQ_ERR_ALIGN
+    assert _rtn_encode(codes=MIS) == L.PGKQ_ERR_ALIGN
+    assert _rtn_encode(n_tok=0) == L.PGKQ_OK
+
+
+def _rtn_decode(d=128, bits=4, q=A, qd=L.PGKQ_BF16, n_seq=2, n_q=8, n_kv=2, n_tok=100, cap=128,
+                codes=A, V=A, out=A, ws=A, wsb=1 << 30, n_splits=0):
+    o = L.PgkqLaunchOpts(n_splits, None, None)
+    return L.lib().pgkq_rtn_decode_attn(d, bits, _vp(q) if q else None, qd, n_seq, n_q, n_kv, n_tok,
+                                        cap, _vp(codes) if codes else None, _vp(V) if V else None,
+                                        _vp(out) if out else None, 0.0, ctypes.byref(o),
+                                        _vp(ws) if ws else None, wsb, None)
+
+
+def test_rtn_decode_validation():
+    assert _rtn_decode(q=0) == L.PGKQ_ERR_NULL
+    assert _rtn_decode(codes=0) == L.PGKQ_ERR_NULL
+    assert _rtn_decode(V=0) == L.PGKQ_ERR_NULL
+    assert _rtn_decode(out=0) == L.PGKQ_ERR_NULL
+    assert _rtn_decode(ws=0) == L.PGKQ_ERR_NULL
+    assert _rtn_decode(bits=5) == L.PGKQ_ERR_UNSUPPORTED
+    assert _rtn_decode(n_q=6) == L.PGKQ_ERR_UNSUPPORTED
+    assert _rtn_decode(n_q=7) == L.PGKQ_ERR_SHAPE
+    assert _rtn_decode(n_tok=129) == L.PGKQ_ERR_SHAPE
+    assert _rtn_decode(cap=1 << 24) == L.PGKQ_ERR_SHAPE
+    assert _rtn_decode(qd=9) == L.PGKQ_ERR_UNSUPPORTED
+    assert _rtn_decode(V=MIS) == L.PGKQ_ERR_ALIGN
+    assert _rtn_decode(codes=MIS) == L.PGKQ_ERR_ALIGN
+    need = api.pgkq_rtn_decode_workspace_bytes(128, 2, 8, 2, 100)
+    assert need > 0
+    assert _rtn_decode(wsb=need - 1) == L.PGKQ_ERR_WORKSPACE
+    st = L.lib().pgkq_rtn_logits(64, 3, _vp(A), L.PGKQ_F32, 1, 4, 4, 10, 16, _vp(A), None, _vp(A),
+                                 1 << 20, None)
+    assert st == L.PGKQ_ERR_NULL
+    # more splits need more workspace
+    w1 = api.pgkq_rtn_decode_workspace_bytes(128, 1, 32, 8, 131072, n_splits=1)
+    w256 = api.pgkq_rtn_decode_workspace_bytes(128, 1, 32, 8, 131072, n_splits=256)
+    assert w256 - w1 >= 32 * 256 * (128 + 4) * 4 - 256

@@ -529,3 +529,89 @@ def test_rtn_reconstruction_error_bound():
             (1 << bits) * np.abs(scale.astype(np.float64))[:, None] * 2 ** -11 + \
             np.abs(zp.astype(np.float64))[:, None] * 2 ** -11
         assert np.all(err <= bound)
+
+
+def test_rtn_record_is_the_printed_bit_budget():
+    """Record bytes * 8 / d reproduce the 3.50 / 4.50 bits per element printed for
+    INT3 / INT4 RTN at d = 64 ('Comparison to simpler baselines')."""
+    g = json.load(open(os.path.join(GOLDEN, "pages_accounting.json")))["rtn"]
+    assert rtn.record_bytes(64, 3) * 8 / 64 == g["int3_bpe"]
+    assert rtn.record_bytes(64, 4) * 8 / 64 == g["int4_bpe"]
+
+
+@pytest.mark.parametrize("d,bits", [(64, 3), (64, 4), (128, 3), (128, 4)])
+def test_rtn_packing_matches_bit_string(d, bits):
+    """Words of the packed stream against an independent construction: the codes
+    written as one LSB-first bit string, cut into 32-bit words."""
+    rng = np.random.default_rng(d * 10 + bits)
+    N, cap, off = 5, 9, 3
+    codes = rng.integers(0, 1 << bits, size=(N, d))
+    scale = rng.uniform(0.01, 2, N).astype(np.float16)
+    zp = rng.uniform(-5, 5, N).astype(np.float16)
+    buf = rtn.pack_stream(codes, scale, zp, bits, cap, token_offset=off)
+    words = buf.view(np.uint32).reshape(-1, cap)
+    nc = d * bits // 32
+    assert words.shape[0] == nc + 1
+    for t in range(N):
+        bitstr = "".join(format(int(c), f"0{bits}b")[::-1] for c in codes[t])
+        assert len(bitstr) == 32 * nc
+        for w in range(nc):
+            assert int(bitstr[32 * w:32 * w + 32][::-1], 2) == words[w, off + t]
+        sz = int(words[nc, off + t])
+        assert sz & 0xFFFF == int(scale[t].view(np.uint16))
+        assert sz >> 16 == int(zp[t].view(np.uint16))
+    assert not words[:, :off].any() and not words[:, off + N:].any()
+    c2, s2, z2 = rtn.unpack_stream(buf, d, bits, cap, N, token_offset=off)
+    assert np.array_equal(c2, codes) and np.array_equal(s2.view(np.uint16), scale.view(np.uint16))
+    assert np.array_equal(z2.view(np.uint16), zp.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_rtn_ramp_is_exact(bits):
+    """A ramp lo + j * step over 2^b levels with an fp16-exact step is its own
+    quantization: zero-point lo, scale step, codes j, exact reconstruction."""
+    L = 1 << bits
+    lo, step = -1.25, 0.375
+    K = (lo + step * (np.arange(64) % L)).reshape(1, 64)
+    codes, scale, zp = rtn.quantize(K, bits)
+    assert float(zp[0]) == lo and float(scale[0]) == step
+    assert np.array_equal(codes[0], np.arange(64) % L)
+    assert np.array_equal(rtn.dequantize(codes, scale, zp), K)
+
+
+def test_rtn_rounds_half_to_even_and_handles_degenerate_keys():
+    # range 15 -> scale 1 at INT4: half-way values go to the even code
+    k = np.zeros(64)
+    k[:8] = [0.0, 0.5, 1.5, 2.5, 3.5, 14.5, 15.0, 7.5]
+    codes, scale, zp = rtn.quantize(k[None], 4)
+    assert float(scale[0]) == 1.0 and float(zp[0]) == 0.0
+    assert list(codes[0, :8]) == [0, 0, 2, 2, 4, 14, 15, 8]
+    # a constant key: zero range -> scale 1, every code 0, exact reconstruction
+    c = np.full((1, 64), -3.0)
+    codes, scale, zp = rtn.quantize(c, 3)
+    assert float(scale[0]) == 1.0 and not codes.any()
+    assert np.array_equal(rtn.dequantize(codes, scale, zp), c)
+    # -0 and +0 extremes give the +0 zero-point
+    z = np.zeros((1, 64))
+    z[0, 5] = -0.0
+    _, _, zp = rtn.quantize(z, 3)
+    assert zp[0].view(np.uint16) == 0
+    # a minimum that fp16 rounds upward is clamped to code 0, not -1
+    m = np.linspace(0, 1, 64)
+    m[0] = 1e-3 + 2 ** -22  # fp16(m0) > m0
+    codes, _, zp = rtn.quantize(m[None], 4)
+    assert float(zp[0]) > m[0] and codes[0, 0] == 0
+
+
+def test_rtn_logits_converge_to_exact_with_bits():
+    """The RTN logit error shrinks about 2x per extra bit (uniform step)."""
+    rng = np.random.default_rng(3)
+    K = rng.standard_normal((300, 64))
+    q = rng.standard_normal(64)
+    errs = []
+    for bits in (3, 4, 6, 8):
+        codes, scale, zp = rtn.quantize(K, bits)
+        errs.append(np.abs(rtn.logits(q, codes, scale, zp) - K @ q).mean())
+    assert errs[0] > errs[1] > errs[2] > errs[3]
+    assert 1.5 < errs[0] / errs[1] < 2.8
+    assert 10 < errs[1] / errs[3] < 24
