@@ -102,10 +102,86 @@ def cpu_baseline(cfg, inp, budget_s: float = 8.0):
     return res
 
 
+def measure_copy(torch, dev, reps: int = 10):
+    """Practical streaming bandwidths on this GPU beside the 8 TB/s spec figure
+    (GB/s): a 1 GiB device-to-device copy (bytes read + written) and a 1 GiB
+    read-only reduction."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b.copy_(a)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    copy = 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
+    # read-only stream: a sum over the same 1 GiB (int64 accumulation of int32 words)
+    w = a.view(torch.int32)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        w.sum(dtype=torch.int64)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b, w
+    return copy, n / (float(np.median(ts)) * 1e-3) / 1e9
+
+
+def run_controls(api, torch, dev, cfg, K, V, q, flush, E, reps: int = 20):
+    """The same decode workload on the RTN INT4 / INT3 key caches and on the
+    uncompressed fp16 cache (same keys, values, queries and split count): scan
+    kernel time and its share of the HBM peak."""
+    n_seq, n_kv, T, d = K.shape
+    res = {}
+    e0, e1 = E(), E()
+    e0.record()
+    e1.record()
+
+    def timed(call):
+        ts = []
+        for r in range(reps + 3):
+            flush.fill_(r & 255)
+            call()
+            torch.cuda.synchronize()
+            if r >= 3:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    out = torch.empty((n_seq, cfg.n_q, d), dtype=torch.float32, device=dev)
+    for bits in (4, 3):
+        rb = api.pgkq_rtn_record_bytes(d, bits)
+        codes = api.pgkq_rtn_encode(K, bits)
+        ws = torch.empty(api.pgkq_rtn_decode_workspace_bytes(d, n_seq, cfg.n_q, n_kv, T, cfg.n_splits),
+                         dtype=torch.uint8, device=dev)
+        ms = timed(lambda: api.pgkq_rtn_decode_attn(q, codes, V, bits, n_splits=cfg.n_splits, out=out,
+                                                    workspace=ws, events=(e0, e1)))
+        alg = n_seq * n_kv * T * (rb + 2 * d)
+        res[f"rtn_int{bits}"] = {"record_bytes": rb, "scan_ms": ms,
+                                 "cache_tokens_per_s_scan": n_seq * T / (ms * 1e-3),
+                                 "scan_gbs": alg / (ms * 1e-3) / 1e9,
+                                 "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del codes, ws
+    ws = torch.empty(max(api.pgkq_fp16_decode_workspace_bytes(d, n_seq, cfg.n_q, n_kv, T, cfg.n_splits), 256),
+                     dtype=torch.uint8, device=dev)
+    ms = timed(lambda: api.pgkq_fp16_decode_attn(q, K, V, n_splits=cfg.n_splits, out=out, workspace=ws,
+                                                 events=(e0, e1)))
+    alg = n_seq * n_kv * T * 4 * d
+    res["fp16_cache"] = {"record_bytes": 2 * d, "scan_ms": ms,
+                         "cache_tokens_per_s_scan": n_seq * T / (ms * 1e-3),
+                         "scan_gbs": alg / (ms * 1e-3) / 1e9,
+                         "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
@@ -189,6 +265,10 @@ def main():
                     e[5].elapsed_time(e[6])] for e in evs])  # ms
     cal_ms, enc_ms, dec_ms, scan_ms = (float(np.median(ph[:, k])) for k in range(4))
     scan_mean = float(np.mean(ph[:, 3]))
+    pct = lambda k: {"p10": float(np.percentile(ph[:, k], 10)), "p50": float(np.median(ph[:, k])),  # noqa: E731
+                     "p90": float(np.percentile(ph[:, k], 90))}
+    copy_gbs, read_gbs = measure_copy(torch, dev)
+    controls = run_controls(api, torch, dev, cfg, K, V, q, flush, E)
 
     token_heads = n_seq * n_kv * T
     alg_bytes = token_heads * (rb + 2 * d)
@@ -227,6 +307,8 @@ def main():
         },
         "phases_ms": {"calibrate": cal_ms, "encode": enc_ms, "decode_attn": dec_ms,
                       "decode_scan_kernel": scan_ms},
+        "phase_percentiles_ms": {"decode_attn": pct(2), "decode_scan_kernel": pct(3),
+                                 "encode": pct(1)},
         "decode": {"cache_tokens_per_s": value, "token_heads_per_s": token_heads / (dec_ms * 1e-3),
                    "algorithmic_bytes": alg_bytes,
                    "gbs_whole_call": alg_bytes / (dec_ms * 1e-3) / 1e9},
@@ -241,7 +323,10 @@ def main():
                                 "note": "VALU-bound (float64 transform and code decisions)"}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean},
+                     "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean,
+                     "measured_copy_gbs": copy_gbs, "measured_read_gbs": read_gbs,
+                     "frac_of_measured_read": achieved / read_gbs},
+        "controls": controls,
     }
     if not args.no_cpu_baseline:
         cb_res = cpu_baseline(cfg, inp)

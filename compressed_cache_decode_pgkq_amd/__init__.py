@@ -10,12 +10,14 @@ C entry points.
 from .api import (  # noqa: F401
     PgkqParams,
     pgkq_calibrate,
+    pgkq_calibrate_workspace_bytes,
     pgkq_codes_bytes,
     pgkq_decode_attn,
     pgkq_decode_workspace_bytes,
     pgkq_encode,
     pgkq_estimate_logits,
     pgkq_fp16_decode_attn,
+    pgkq_fp16_decode_workspace_bytes,
     pgkq_lloyd_max_beta,
     pgkq_record_bytes,
     pgkq_rtn_decode_attn,
@@ -23,6 +25,7 @@ from .api import (  # noqa: F401
     pgkq_rtn_encode,
     pgkq_rtn_logits,
     pgkq_rtn_record_bytes,
+    pgkq_status_string,
     pgkq_version,
 )
 from ._lib import PgkqError  # noqa: F401

@@ -170,6 +170,21 @@ def pgkq_estimate_logits(params: PgkqParams, q: torch.Tensor, codes: torch.Tenso
     return logits
 
 
+def pgkq_fp16_decode_workspace_bytes(head_dim, n_seq, n_q, n_kv, n_tokens, n_splits=0) -> int:
+    o = _opts(n_splits, None)
+    return int(L.lib().pgkq_fp16_decode_workspace_bytes(head_dim, n_seq, n_q, n_kv, n_tokens,
+                                                         ctypes.byref(o)))
+
+
+def pgkq_calibrate_workspace_bytes(params: PgkqParams, n_seq, n_kv, n_tokens) -> int:
+    return int(L.lib().pgkq_calibrate_workspace_bytes(ctypes.byref(params.c()), n_seq, n_kv,
+                                                       n_tokens))
+
+
+def pgkq_status_string(status: int) -> str:
+    return L.status_string(status)
+
+
 def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor, n_tokens=None,
                           softmax_scale: float = 0.0, n_splits: int = 0, out=None, workspace=None,
                           events=None, stream=None):

@@ -1,10 +1,18 @@
 // FP16-cache decode attention for gfx950: the uncompressed comparator the
 // EdgeLLM-Nano page measures fidelity against (its "FP16 wrapper" cache).
 //
-// Same split/online-softmax skeleton as the PGKQ scan: per (sequence, kv-head,
-// token split) workgroup, lane = token for the scores (fp32 dot products of the
-// fp16 key row with the G query heads held in LDS), then the shared softmax and
-// P.V tail.  The query scale is applied as a log2-domain softmax scale.
+// Same split / online-softmax skeleton as the PGKQ scan, but the keys are read
+// exactly like the values: a 16-lane group (8 at d = 64) holds one 256-byte key
+// row, lane k the 8 channels [8k, 8k + 8), so every load instruction reads
+// whole rows.  The lane's slice of the G query heads stays in registers for the
+// whole scan.  Each lane forms the partial dot products of its 8 channels for
+// the rows of the chunk; the partials of a row are then summed across its lane
+// group by a reduce-scatter butterfly: at each level a lane keeps one half of
+// its rows, sends the other half to a partner lane (DPP: xor 1, xor 2, the
+// half-row mirror, the 8-lane rotation) and adds what it receives.  After the
+// last level lane k holds the full scores of one row, which feed the shared
+// softmax and fp16 P.V tail.  Queries are applied as a log2-domain softmax
+// scale.
 #include "softmax_pv.hpp"
 
 namespace pgkq {
@@ -14,70 +22,160 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
+// DPP exchanges inside a 16-lane row: partner masks 1, 2, 7 (half-row mirror)
+// and 8 (rotation by 8); linearly independent over GF(2)^4.
+template <int LEVEL>
+__device__ __forceinline__ float dpp_partner(float v) {
+  constexpr int ctrl = LEVEL == 0 ? 0xB1 : LEVEL == 1 ? 0x4E : LEVEL == 2 ? 0x141 : 0x128;
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true));
+}
+
+// Row kept at each level: the dual basis of the partner masks (1, 2, 7, 8):
+// f0 = k0 ^ k2, f1 = k1 ^ k2, f2 = k2, f3 = k3 (bit j of the lane index k).
+__device__ __forceinline__ int keep_bits(int k) {
+  const int k0 = k & 1, k1 = (k >> 1) & 1, k2 = (k >> 2) & 1, k3 = (k >> 3) & 1;
+  return (k0 ^ k2) | ((k1 ^ k2) << 1) | (k2 << 2) | (k3 << 3);
+}
+
+// 8 query heads at d = 128 hold 64 query and 64 accumulator registers per lane:
+// one wavefront per SIMD, so that the register file (and AGPRs) has room.
 template <int D, int G>
-__global__ void __launch_bounds__(kThreads)
+constexpr int fp16_min_waves() { return G * D > 512 ? 1 : 2; }
+
+template <int D, int G, bool WAVE_PARTS>
+__global__ void __launch_bounds__(kThreads, (fp16_min_waves<D, G>()))
 fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* __restrict__ V) {
-  constexpr int MERGE_FLOATS = SoftmaxPV<D, G, kWaves>::MERGE_FLOATS;
-  constexpr int QF = G * D;
-  constexpr int MAIN = QF > MERGE_FLOATS ? QF : MERGE_FLOATS;
-  __shared__ __align__(16) float s_main[MAIN];  // queries, then the merge
+  using SM = SoftmaxPV<D, G, kWaves>;
+  constexpr int NIT = kWave / SM::TPI;  // rows per lane group per chunk (16 or 8)
+  constexpr int LEVELS = NIT == 16 ? 4 : 3;
+  __shared__ __align__(16) float s_merge[SM::MERGE_FLOATS];
   __shared__ __align__(16) float s_p[kWaves][kWave][G];
 
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
   const int h = blockIdx.y;
   const int64_t b = blockIdx.z;
-  // s_main[c * G + g] = q of head h*G + g, channel c
-  for (int e = tid; e < QF; e += kThreads) {
-    const int g = e % G, c = e / G;
-    s_main[e] = load_f(a.q, a.q_dtype, (size_t(b) * a.n_q + size_t(h) * G + g) * D + c);
-  }
-  __syncthreads();
+
+  SM sm;
+  sm.init(tid);
+  const int lane = sm.lane, wave = sm.wave, k = sm.dblk, slot = sm.slot;
+
+  // this lane's 8 channels of every query head of the group
+  float qr[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      qr[g][j] = load_f(a.q, a.q_dtype, (size_t(b) * a.n_q + size_t(h) * G + g) * D + 8 * k + j);
+
+  const int kb = keep_bits(k);
+  const int my_row = kb & (NIT - 1);          // row of the chunk this lane ends up scoring
+  const int prow = my_row * SM::TPI + slot;   // its token index within the chunk
 
   const int64_t t_begin = int64_t(split) * a.tokens_per_split;
   const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
-  const __half* kbase = K + size_t(stream) * a.capacity * D;
-  const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
+  const uint32_t range = static_cast<uint32_t>(t_end * D * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + size_t(stream) * a.capacity * D, range);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + size_t(stream) * a.capacity * D, range);
 
-  SoftmaxPV<D, G, kWaves> sm;
-  sm.init(tid);
-  for (int64_t c0 = t_begin + int64_t(sm.wave) * kWave; c0 < t_end; c0 += kThreads) {
-    const int64_t t = c0 + sm.lane;
-    const bool valid = t < t_end;
-    typename SoftmaxPV<D, G, kWaves>::VChunk vc;
-    sm.load_v(vc, c0, vrs);
+  int64_t c_first, c_end, c_step;
+  if constexpr (WAVE_PARTS) {
+    const int64_t tpw = a.tokens_per_split / kWaves;
+    c_first = t_begin + int64_t(wave) * tpw;
+    c_end = min<int64_t>(c_first + tpw, t_end);
+    c_step = kWave;
+  } else {
+    c_first = t_begin + int64_t(wave) * kWave;
+    c_end = t_end;
+    c_step = kThreads;
+  }
+  for (int64_t c0 = c_first; c0 < c_end; c0 += c_step) {
+    // key rows: same layout as the value rows.  With 8 query heads at d = 128
+    // the key rows come in two halves and the value rows are requested after
+    // the scores (registers).
+    constexpr bool kSplitK = G * D > 512;
+    constexpr int KPARTS = kSplitK ? 2 : 1;
+    constexpr int KROWS = NIT / KPARTS;
+    const uint32_t kbase = static_cast<uint32_t>(c0 + slot) * (D * 2) + k * 16;
+    typename SM::VChunk vc;
+    u32x4 kr[KROWS];
+#pragma unroll
+    for (int r = 0; r < KROWS; ++r) kr[r] = buf_load_b128(krs, kbase + r * SM::TPI * D * 2);
+    if constexpr (!kSplitK) sm.load_v(vc, c0, vrs);
+
+    // partial dot products of row `it` (8 channels), reduced level by level as
+    // soon as both halves of a level exist: at most LEVELS + 1 live per head
+    float part[G][LEVELS + 1];
     float s[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.f;
-    if (valid) {
-      const uint4* krow = reinterpret_cast<const uint4*>(kbase + size_t(t) * D);
-#pragma unroll 4
-      for (int c8 = 0; c8 < D / 8; ++c8) {
-        const uint4 raw = krow[c8];
-        const __half2* hk = reinterpret_cast<const __half2*>(&raw);
+    for (int it = 0; it < NIT; ++it) {
+      if (kSplitK && it == KROWS) {
+        sched_fence();
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float2 f2 = __half22float2(hk[k]);
-          float q0[G], q1[G];
-          lds_fetch<G>(&s_main[(c8 * 8 + 2 * k) * G], q0);
-          lds_fetch<G>(&s_main[(c8 * 8 + 2 * k + 1) * G], q1);
+        for (int r = 0; r < KROWS; ++r)
+          kr[r] = buf_load_b128(krs, kbase + (KROWS + r) * SM::TPI * D * 2);
+      }
+      __half2 hk[4];
+      __builtin_memcpy(hk, &kr[it % KROWS], sizeof(hk));
+      float dot[G];
 #pragma unroll
-          for (int g = 0; g < G; ++g) s[g] = fmaf(f2.y, q1[g], fmaf(f2.x, q0[g], s[g]));
+      for (int g = 0; g < G; ++g) dot[g] = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float2 f = __half22float2(hk[j]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) dot[g] = fmaf(f.y, qr[g][2 * j + 1], fmaf(f.x, qr[g][2 * j], dot[g]));
+      }
+      // carry the new leaf up the tree: level L combines when bit L of it
+      // completes a pair of blocks
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float v = dot[g];
+        int lvl = 0;
+#pragma unroll
+        for (int L = 0; L < LEVELS; ++L) {
+          if (lvl == L && ((it >> L) & 1)) {
+            const bool keep_hi = (kb >> L) & 1;
+            const float lo = part[g][L], hi = v;
+            const float keep = keep_hi ? hi : lo;
+            const float send = keep_hi ? lo : hi;
+            const float recv = L == 0 ? dpp_partner<0>(send)
+                             : L == 1 ? dpp_partner<1>(send)
+                             : L == 2 ? dpp_partner<2>(send)
+                                      : dpp_partner<3>(send);
+            v = keep + recv;
+            lvl = L + 1;
+          }
         }
+        if (lvl < LEVELS) part[g][lvl] = v;
+        else s[g] = v;
       }
     }
-    sm.chunk(s, valid, a.scale_log2, vc, &s_p[sm.wave][0][0]);
+    if constexpr (kSplitK) {
+      sched_fence();  // keep the value loads behind the key registers' last use
+      sm.load_v(vc, c0, vrs);
+    }
+    const bool valid = c0 + prow < c_end;
+    sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], prow);
   }
-  __syncthreads();
-  sm.finish(s_main, tid, a.n_splits, split, a.out, a.partial, size_t(b) * a.n_q + size_t(h) * G);
+  const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
+  if constexpr (WAVE_PARTS) {
+    sm.finish_wave(a.partial, row0, split * kWaves + wave, a.n_splits * kWaves);
+  } else {
+    __syncthreads();
+    sm.finish(s_merge, tid, a.n_splits, split, a.out, a.partial, row0);
+  }
 }
 
 template <int D, int G>
 hipError_t fp16_t(const Fp16DecodeArgs& a, hipStream_t s) {
   dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
-  hipLaunchKernelGGL((fp16_scan_kernel<D, G>), grid, dim3(kThreads), 0, s, a, a.K, a.V);
+  if (a.wave_parts) {
+    hipLaunchKernelGGL((fp16_scan_kernel<D, G, true>), grid, dim3(kThreads), 0, s, a, a.K, a.V);
+  } else {
+    hipLaunchKernelGGL((fp16_scan_kernel<D, G, false>), grid, dim3(kThreads), 0, s, a, a.K, a.V);
+  }
   return hipGetLastError();
 }
 

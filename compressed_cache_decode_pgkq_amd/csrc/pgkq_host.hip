@@ -115,8 +115,8 @@ size_t decode_ws(const Geometry& g, int64_t n_seq, int64_t n_q, const Splits& sp
 }
 
 size_t fp16_ws(int d, int64_t n_seq, int64_t n_q, const Splits& sp) {
-  if (sp.n <= 1) return 0;
-  return round_up(size_t(n_seq) * n_q * sp.n * (d + 4) * sizeof(float), 256);
+  if (sp.partials() <= 1) return 0;
+  return round_up(size_t(n_seq) * n_q * sp.partials() * (d + 4) * sizeof(float), 256);
 }
 
 __global__ void zero_fill_kernel(float* p, size_t n) {
@@ -497,7 +497,7 @@ size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t
   if ((head_dim != 64 && head_dim != 128) || n_seq < 1 || n_q < 1 || n_kv < 1 || n_tokens < 0)
     return 0;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
-                                  opts ? opts->n_splits : 0, false);
+                                  opts ? opts->n_splits : 0);
   return fp16_ws(head_dim, n_seq, n_q, sp);
 }
 
@@ -519,7 +519,7 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
       (workspace && !aligned16(workspace)))
     return PGKQ_ERR_ALIGN;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
-                                  opts ? opts->n_splits : 0, false);
+                                  opts ? opts->n_splits : 0);
   const size_t need = fp16_ws(head_dim, n_seq, n_q, sp);
   if (need && (!workspace || workspace_bytes < need)) return PGKQ_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -540,6 +540,7 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   a.partial = static_cast<float*>(workspace);
   a.n_splits = sp.n;
   a.tokens_per_split = sp.tokens_per;
+  a.wave_parts = sp.wave_parts;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   a.scale_log2 = scale * 1.4426950408889634f;
   if (opts && opts->scan_start) {
@@ -552,7 +553,8 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
     if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
       return PGKQ_ERR_HIP;
   }
-  if (sp.n > 1) return map_hip(pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.n, a.partial, out, s));
+  if (sp.partials() > 1)
+    return map_hip(pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.partials(), a.partial, out, s));
   return PGKQ_OK;
 }
 

@@ -99,6 +99,7 @@ struct Fp16DecodeArgs {
   float* partial;
   int n_splits;
   int64_t tokens_per_split;
+  int wave_parts;       // 1: each wavefront scans its own partition
   float scale_log2;
 };
 

@@ -75,10 +75,15 @@ struct SoftmaxPV {
     for (int it = 0; it < kWave / TPI; ++it) vc.r[it] = buf_load_b128(vr, base + it * TPI * D * 2);
   }
 
-  // s: raw scores of token c0 + lane (ignored when !valid); p_rows: this
-  // wavefront's [64][G] LDS rows.
+  // s: raw scores of token c0 + prow (ignored when !valid); p_rows: this
+  // wavefront's [64][G] LDS rows.  prow is a permutation of the lanes (the
+  // lane index when scores arrive lane = token).
   __device__ __forceinline__ void chunk(const float (&s)[G], bool valid, float scale_log2,
                                         const VChunk& vc, float* p_rows) {
+    chunk(s, valid, scale_log2, vc, p_rows, lane);
+  }
+  __device__ __forceinline__ void chunk(const float (&s)[G], bool valid, float scale_log2,
+                                        const VChunk& vc, float* p_rows, int prow) {
     float pv[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -95,13 +100,13 @@ struct SoftmaxPV {
       l_lane[g] += pv[g];
     }
     if constexpr (G == 1) {
-      p_rows[lane] = pv[0];
+      p_rows[prow] = pv[0];
     } else if constexpr (G == 2) {
-      *reinterpret_cast<float2*>(p_rows + lane * 2) = make_float2(pv[0], pv[1]);
+      *reinterpret_cast<float2*>(p_rows + prow * 2) = make_float2(pv[0], pv[1]);
     } else {
 #pragma unroll
       for (int g = 0; g < G; g += 4)
-        *reinterpret_cast<float4*>(p_rows + lane * G + g) = make_float4(pv[g], pv[g + 1], pv[g + 2], pv[g + 3]);
+        *reinterpret_cast<float4*>(p_rows + prow * G + g) = make_float4(pv[g], pv[g + 1], pv[g + 2], pv[g + 3]);
     }
     wave_lds_sync();
 #pragma unroll

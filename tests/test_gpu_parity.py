@@ -235,22 +235,54 @@ def test_end_to_end_calibrate_encode_decode():
     assert err <= OUT_TOL
 
 
-@pytest.mark.parametrize("name", ["c2a", "c3"])
-def test_fp16_comparator_matches_oracle(name):
+def _fp16_check(cfg, n_splits=0, T=None, cap=None):
+    from synth import make_inputs
     api = _api()
-    cfg, _ = SMALL[name]
-    case = Case(cfg)
-    n_seq, n_kv, T, d = case.K.shape
-    K16 = case.K.astype(np.float16)
-    Kp = np.zeros((n_seq, n_kv, case.cap, d), np.float16)
+    inp = make_inputs(cfg)
+    T = cfg.n_tokens if T is None else T
+    cap = T if cap is None else cap
+    n_seq, n_kv = cfg.n_seq, cfg.n_kv
+    d = cfg.head_dim
+    K16 = inp["K"][:, :, :T].astype(np.float16)
+    V16 = inp["V"][:, :, :T]
+    Kp = np.zeros((n_seq, n_kv, cap, d), np.float16)
+    Vp = np.zeros((n_seq, n_kv, cap, d), np.float16)
     Kp[:, :, :T] = K16
-    dev = case.dev_inputs()
-    out = api.pgkq_fp16_decode_attn(q_tensor(case.q, cfg.q_dtype), to_dev(Kp), dev["V"], n_tokens=T)
+    Vp[:, :, :T] = V16
+    out = api.pgkq_fp16_decode_attn(q_tensor(inp["q"], cfg.q_dtype), to_dev(Kp), to_dev(Vp),
+                                    n_tokens=T, n_splits=n_splits)
     torch.cuda.synchronize()
-    ref, _ = attn.fp16_attention(case.q, K16, case.V)
+    ref, _ = attn.fp16_attention(inp["q"], K16, V16)
     err = float(np.max(np.abs(out.cpu().numpy() - ref)))
-    print("fp16 comparator max-abs", err)
+    print("fp16 comparator max-abs", cfg.name, n_splits, T, err)
     assert err <= OUT_TOL
+
+
+@pytest.mark.parametrize("n_splits", [0, 1, 5, 40])
+@pytest.mark.parametrize("name", ["c2a", "c3"])
+def test_fp16_comparator_matches_oracle(name, n_splits):
+    cfg, _ = SMALL[name]
+    _fp16_check(cfg, n_splits)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp16_comparator_group_sizes(d, group):
+    base = CONFIGS["c2a"] if d == 64 else CONFIGS["c3"]
+    cfg = base.with_(n_seq=1, n_kv=4, n_q=4 * group, n_tokens=700)
+    _fp16_check(cfg, 0)
+    _fp16_check(cfg, 6)
+
+
+@pytest.mark.parametrize("T", [1, 63, 65, 777])
+def test_fp16_comparator_ragged(T):
+    cfg = CONFIGS["c3"].with_(n_seq=1, n_tokens=1000)
+    for ns in (0, 3, 9):
+        _fp16_check(cfg, ns, T=T, cap=1024)
+
+
+def test_fp16_comparator_long_stream_wave_partitions():
+    _fp16_check(CONFIGS["c5"].with_(n_tokens=6000), 0)
 
 
 # ------------------------------------------------------------------ negative controls
