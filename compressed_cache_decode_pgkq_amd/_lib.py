@@ -67,6 +67,9 @@ SIGNATURES = {
     "pgkq_decode_workspace_bytes": (_sz, [_P, _i64, _i64, _i64, _i64, _O]),
     "pgkq_decode_attn": (ctypes.c_int, [_P, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _f32, _O, _vp, _sz, _vp]),
+    "pgkq_decode_step": (ctypes.c_int, [_P, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _i64, _i64,
+                                        _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _O,
+                                        _vp, _sz, _vp]),
     "pgkq_estimate_logits": (ctypes.c_int, [_P, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pgkq_fp16_decode_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _O]),

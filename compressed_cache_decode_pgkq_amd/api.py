@@ -152,6 +152,30 @@ def pgkq_decode_attn(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, V
     return out
 
 
+def pgkq_decode_step(params: PgkqParams, q: torch.Tensor, k_new: torch.Tensor,
+                     v_new: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, n_cached: int,
+                     signs, perm, codebook, S, softmax_scale: float = 0.0, n_splits: int = 0,
+                     out=None, workspace=None, events=None, stream=None):
+    """Append k_new, v_new [n_seq, n_kv, d] at slot n_cached of codes / V (in place),
+    then decode attention over n_cached + 1 tokens -> out [n_seq, n_q, d]."""
+    n_seq, n_q, d = q.shape
+    n_kv, cap = V.shape[1], V.shape[2]
+    p = params.c()
+    o = _opts(n_splits, events)
+    if out is None:
+        out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    nb = int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(p), n_seq, n_q, n_kv,
+                                                  int(n_cached) + 1, ctypes.byref(o)))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_decode_step(ctypes.byref(p), _ptr(q), _dtype(q), _ptr(k_new), _dtype(k_new),
+                                  _ptr(v_new), n_seq, n_q, n_kv, int(n_cached), cap, _ptr(signs),
+                                  _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes), _ptr(V),
+                                  _ptr(out), float(softmax_scale), ctypes.byref(o), _ptr(ws), wsb,
+                                  _stream(stream))
+    L.check(st, "pgkq_decode_step")
+    return out
+
+
 def pgkq_estimate_logits(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, n_kv: int,
                          capacity: int, signs, perm, codebook, S, n_tokens=None, logits=None,
                          workspace=None, stream=None):

@@ -41,6 +41,114 @@ constexpr int kScanMinWavesPerEU = PGKQ_SCAN_MIN_WAVES;
 constexpr int kPairGroup = PGKQ_PAIR_GROUP;
 
 
+// ------------------------------------------------------------------ append
+
+// Encode one new key of stream (b, h) into slot a.append_slot and copy its
+// value row: steps (1)-(4) of the pipeline for a single key, by the 128
+// threads of a query-prep workgroup.  Decisions are taken on the unnormalized
+// transform X = sqrt(d) k~ (exact in float64 for fp16 keys): X_x^2 + X_y^2
+// against d T_j^2 and the octant comparisons of (X_x, X_y), as in the bulk
+// encoder; the residual, its norm and the QJL projection are float64.
+template <int D, int BM, bool QJL>
+__device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int64_t b, int h,
+                           int tid) {
+  constexpr int N = D / 2;
+  constexpr int BA = BM - 1;
+  constexpr int P = BM + BA;
+  constexpr int L = 1 << BM;
+  constexpr int A = 1 << BA;
+  constexpr int M = QJL ? D : 0;
+  constexpr int NC = N * P / 32;
+  constexpr int NSW = M / 32;
+  __shared__ double s_x[D];
+  __shared__ double s_ss[N];
+  __shared__ uint32_t s_code[N];
+  __shared__ uint32_t s_bit[D];
+  const int64_t stream = b * a.n_kv + h;
+  const float* cb = a.codebook + size_t(h) * 2 * L;
+  if (tid < D) {
+    const int src = a.perm ? int(a.perm[size_t(h) * D + tid]) : tid;
+    double v = static_cast<double>(load_f(a.k_new, a.k_dtype, size_t(stream) * D + src));
+    if (a.hadamard && a.signs[size_t(h) * D + tid] < 0) v = -v;
+    s_x[tid] = v;
+  }
+  __syncthreads();
+  if (a.hadamard) {
+    for (int hh = 1; hh < D; hh <<= 1) {
+      double u = 0.0, w = 0.0;
+      int c0 = 0;
+      if (tid < D / 2) {
+        c0 = (tid / hh) * 2 * hh + (tid % hh);
+        u = s_x[c0];
+        w = s_x[c0 + hh];
+      }
+      __syncthreads();
+      if (tid < D / 2) {
+        s_x[c0] = u + w;
+        s_x[c0 + hh] = u - w;
+      }
+      __syncthreads();
+    }
+  }
+  if (tid < N) {
+    const double x = s_x[2 * tid], y = s_x[2 * tid + 1];
+    const double r2 = x * x + y * y;
+    const double tscale = a.hadamard ? double(D) : 1.0;
+    int rc = 0;
+#pragma unroll
+    for (int j = 0; j < L - 1; ++j) {
+      const double t = static_cast<double>(cb[L + j]);
+      rc += (tscale * t * t < r2) ? 1 : 0;
+    }
+    const int ac = octant_cell(x, y) >> (3 - BA);
+    s_code[tid] = static_cast<uint32_t>(rc | (ac << BM));
+    if constexpr (QJL) {
+      const double inv_scale = a.hadamard ? 1.0 / sqrt(double(D)) : 1.0;
+      double sn, cs;
+      sincospi(-1.0 + (2.0 * ac + 1.0) / double(A), &sn, &cs);
+      const double lv = static_cast<double>(cb[rc]);
+      const double ex = x * inv_scale - lv * cs;
+      const double ey = y * inv_scale - lv * sn;
+      s_x[2 * tid] = ex;   // this thread's own pair: no other reader yet
+      s_x[2 * tid + 1] = ey;
+      s_ss[tid] = ex * ex + ey * ey;
+    }
+  }
+  __syncthreads();
+  if constexpr (QJL) {
+    if (tid < M) {
+      const float* Sr = S + (size_t(h) * M + tid) * D;
+      double u = 0.0;
+      for (int c = 0; c < D; ++c) u += static_cast<double>(Sr[c]) * s_x[c];
+      s_bit[tid] = u >= 0.0 ? 1u : 0u;
+    }
+    __syncthreads();
+  }
+  const int64_t slot = a.append_slot;
+  uint8_t* base = a.codes_w + size_t(stream) * a.stream_bytes;
+  uint32_t* rows = reinterpret_cast<uint32_t*>(base);
+  if (tid < NC) {
+    uint32_t word = 0;
+    for (int i = (32 * tid) / P; i <= (32 * tid + 31) / P && i < N; ++i) {
+      const int o = P * i - 32 * tid;
+      word |= o >= 0 ? (s_code[i] << o) : (s_code[i] >> (-o));
+    }
+    rows[size_t(tid) * a.capacity + slot] = word;
+  } else if (QJL && tid < NC + NSW) {
+    const int w = tid - NC;
+    uint32_t word = 0;
+    for (int j = 0; j < 32; ++j) word |= s_bit[32 * w + j] << j;
+    rows[size_t(tid) * a.capacity + slot] = word;
+  }
+  if (QJL && tid == 0) {
+    double ss = 0.0;
+    for (int i = 0; i < N; ++i) ss += s_ss[i];
+    uint16_t* nu = reinterpret_cast<uint16_t*>(base + size_t(4) * (NC + NSW) * a.capacity);
+    nu[slot] = f64_to_f16_rne_sat_nonneg(sqrt(ss));
+  }
+  if (tid < D) a.V_w[(size_t(stream) * a.capacity + slot) * D + tid] = a.v_new[size_t(stream) * D + tid];
+}
+
 // ------------------------------------------------------------------ query prep
 
 template <int D, int BM, bool QJL>
@@ -55,6 +163,9 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
   const int hq = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int h = hq / a.group;
+
+  // decode step: the first query head of each kv-head appends its new token
+  if (a.append_slot >= 0 && hq % a.group == 0) append_key<D, BM, QJL>(a, S, b, h, tid);
 
   __shared__ float sx[D];
   __shared__ double sq64[D];

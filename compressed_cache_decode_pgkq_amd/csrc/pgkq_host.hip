@@ -74,10 +74,12 @@ struct Splits {
 
 constexpr int kScanWaves = 4;
 
-// Partitions of the token axis per (sequence, kv-head).  Automatic: about
-// 2048 wavefronts of work in flight.  With many streams, workgroup splits of at
-// least 512 tokens whose wavefronts interleave 64-token chunks; with few long
-// streams (fewer than 64), one partition per wavefront, about 2048 in total.
+// Partitions of the token axis per (sequence, kv-head).  Automatic: with many
+// streams, workgroup splits of at least 512 tokens whose wavefronts interleave
+// 64-token chunks, about 1024 workgroups in total: two rounds of the 512 that
+// are resident at once (2 per CU), which measured faster than one round (a
+// long tail) or four (more table builds); with few long streams (fewer than
+// 64), one partition per wavefront, about 2048 in total.
 // A requested count is honoured as the number of partial states merged per
 // query head; when its partitions are short (at most 1024 tokens) each
 // workgroup runs four consecutive partitions, one per wavefront, sharing one
@@ -97,7 +99,7 @@ Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested,
       return Splits{static_cast<int>(ns), tps, 1};
     }
   }
-  int64_t ns = requested > 0 ? requested : (2048 + n_units - 1) / n_units;
+  int64_t ns = requested > 0 ? requested : (1024 + n_units - 1) / n_units;
   const int64_t min_tokens = requested > 0 ? 64 : 512;
   const int64_t max_ns = std::max<int64_t>(1, (n_tokens + min_tokens - 1) / min_tokens);
   ns = std::min<int64_t>(std::max<int64_t>(ns, 1), max_ns);
@@ -387,16 +389,31 @@ size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t 
   return decode_ws(g, n_seq, n_q, sp);
 }
 
+// The new token of a decode step (pgkq_decode_step): appended at slot `slot`.
+struct StepIn {
+  const void* k_new;
+  pgkq_dtype k_dtype;
+  const void* v_new;
+  int64_t slot;
+};
+
 static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
                                  int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
                                  int64_t capacity, const int8_t* signs, const uint16_t* perm,
                                  const float* codebook, const float* S, const void* codes,
                                  const void* V, float* out, float* logits, float softmax_scale,
                                  const pgkq_launch_opts* opts, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 size_t workspace_bytes, void* stream,
+                                 const StepIn* step = nullptr) {
   Geometry g;
   pgkq_status st = check_params(p, &g);
   if (st != PGKQ_OK) return st;
+  if (step) {
+    if (!step->k_new || !step->v_new) return PGKQ_ERR_NULL;
+    if ((st = check_dtype(step->k_dtype, false)) != PGKQ_OK) return st;
+    if (!aligned16(step->k_new) || !aligned16(step->v_new)) return PGKQ_ERR_ALIGN;
+    if (step->slot < 0 || step->slot + 1 != n_tokens) return PGKQ_ERR_SHAPE;
+  }
   const bool logits_mode = logits != nullptr;
   if (!q || !signs || !codebook || !codes || !workspace) return PGKQ_ERR_NULL;
   if (!logits_mode && (!V || !out)) return PGKQ_ERR_NULL;
@@ -448,6 +465,15 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   a.wave_parts = sp.wave_parts;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(g.d));
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.append_slot = -1;
+  if (step) {
+    a.append_slot = step->slot;
+    a.k_new = step->k_new;
+    a.k_dtype = static_cast<int>(step->k_dtype);
+    a.v_new = static_cast<const __half*>(step->v_new);
+    a.codes_w = static_cast<uint8_t*>(const_cast<void*>(codes));
+    a.V_w = static_cast<__half*>(const_cast<void*>(V));
+  }
   hipError_t e = pgkq::launch_query_prep(g, a, s);
   if (e != hipSuccess) return PGKQ_ERR_HIP;
   if (opts && opts->scan_start) {
@@ -477,6 +503,21 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
   return decode_common(p, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, signs, perm, codebook,
                        S, codes, V, out, nullptr, softmax_scale, opts, workspace, workspace_bytes,
                        stream);
+}
+
+pgkq_status pgkq_decode_step(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                             const void* k_new, pgkq_dtype k_dtype, const void* v_new,
+                             int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_cached,
+                             int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                             const float* codebook, const float* S, void* codes, void* V,
+                             float* out, float softmax_scale, const pgkq_launch_opts* opts,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out || !codes || !V) return PGKQ_ERR_NULL;
+  if (n_cached < 0 || n_cached >= capacity) return PGKQ_ERR_SHAPE;
+  const StepIn step{k_new, k_dtype, v_new, n_cached};
+  return decode_common(p, q, q_dtype, n_seq, n_q, n_kv, n_cached + 1, capacity, signs, perm,
+                       codebook, S, codes, V, out, nullptr, softmax_scale, opts, workspace,
+                       workspace_bytes, stream, &step);
 }
 
 pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,

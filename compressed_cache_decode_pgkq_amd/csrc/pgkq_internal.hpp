@@ -85,6 +85,15 @@ struct DecodeArgs {
   int64_t tokens_per_split;
   int wave_parts;       // 1: each wavefront scans its own partition (n_partials = 4 n_splits)
   float scale_log2;     // softmax scale * log2(e)
+  // decode step: before the scan, the query-prep launch encodes k_new (one key
+  // per stream) into slot append_slot of `codes_w` and copies v_new into the
+  // same slot of `V_w` (append_slot < 0: no append)
+  int64_t append_slot;
+  const void* k_new;
+  int k_dtype;
+  const __half* v_new;
+  uint8_t* codes_w;
+  __half* V_w;
 };
 
 struct Fp16DecodeArgs {

@@ -167,6 +167,24 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
                              const pgkq_launch_opts* opts, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* One decode step of a live cache: append the new token, then attend over it.
+ * Encodes k_new [n_seq][n_kv][d] (k_dtype F32 or F16; steps (1)-(4), one key per
+ * stream) into slot n_cached of every stream of `codes`, copies v_new
+ * [n_seq][n_kv][d] fp16 into slot n_cached of V, then computes decode attention
+ * over tokens [0, n_cached] exactly as pgkq_decode_attn with n_tokens =
+ * n_cached + 1.  The append runs inside the query-preparation launch (no
+ * extra kernel); its decisions are taken in float64 on the unnormalized
+ * transform and its QJL projection is accumulated in float64.  Requires
+ * 0 <= n_cached < capacity; workspace as pgkq_decode_workspace_bytes() for
+ * n_cached + 1 tokens.  codes and V are written (slot n_cached only). */
+pgkq_status pgkq_decode_step(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                             const void* k_new, pgkq_dtype k_dtype, const void* v_new,
+                             int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_cached,
+                             int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                             const float* codebook, const float* S, void* codes, void* V,
+                             float* out, float softmax_scale, const pgkq_launch_opts* opts,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* The attention-logit hook of the throughput paragraph: raw logits (estimates
  * of <q, k_t>, no softmax scale) into logits [n_seq][n_q][n_tokens] fp32.  Same
  * device code as the score step of pgkq_decode_attn.  Workspace as for decode. */

@@ -79,7 +79,7 @@ CONFIGS = {
                           description="NanoGPT-256 full context, B64, d64, T512, b4/3, no QJL"),
     # GQA decode at scale.
     "c3": WorkloadConfig("c3", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,
-                         n_splits=16,
+                         n_splits=8,
                          description="GQA 32q/8kv, d128, T32768, B16, b3/2, QJL m128, split-K"),
     # Bulk encode: the 4 194 304 keys of the c3 cache, with the channel reorder step.
     "c4": WorkloadConfig("c4", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,

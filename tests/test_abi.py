@@ -270,3 +270,28 @@ def test_rtn_decode_validation():
     w1 = api.pgkq_rtn_decode_workspace_bytes(128, 1, 32, 8, 131072, n_splits=1)
     w256 = api.pgkq_rtn_decode_workspace_bytes(128, 1, 32, 8, 131072, n_splits=256)
     assert w256 - w1 >= 32 * 256 * (128 + 4) * 4 - 256
+
+
+def test_decode_step_validation():
+    lib = L.lib()
+    o = L.PgkqLaunchOpts(0, None, None)
+
+    def call(k=A, kd=L.PGKQ_F16, v=A, n_cached=99, cap=128, codes=A, V=A, out=A, wsb=1 << 30):
+        return lib.pgkq_decode_step(_params(128, 3, 2, 128, 1), _vp(A), L.PGKQ_BF16,
+                                    _vp(k) if k else None, kd, _vp(v) if v else None, 2, 8, 2,
+                                    n_cached, cap, _vp(A), None, _vp(A), _vp(A),
+                                    _vp(codes) if codes else None, _vp(V) if V else None,
+                                    _vp(out) if out else None, 0.0, ctypes.byref(o), _vp(A), wsb,
+                                    None)
+
+    assert call(k=0) == L.PGKQ_ERR_NULL
+    assert call(v=0) == L.PGKQ_ERR_NULL
+    assert call(codes=0) == L.PGKQ_ERR_NULL
+    assert call(V=0) == L.PGKQ_ERR_NULL
+    assert call(out=0) == L.PGKQ_ERR_NULL
+    assert call(kd=L.PGKQ_BF16) == L.PGKQ_ERR_UNSUPPORTED
+    assert call(n_cached=128) == L.PGKQ_ERR_SHAPE     # no free slot
+    assert call(n_cached=-1) == L.PGKQ_ERR_SHAPE
+    assert call(k=MIS) == L.PGKQ_ERR_ALIGN
+    assert call(v=MIS) == L.PGKQ_ERR_ALIGN
+    assert call(wsb=16) == L.PGKQ_ERR_WORKSPACE
