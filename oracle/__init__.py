@@ -21,6 +21,8 @@ attn        analytic logits, softmax and FP16-V weighted sum, split/merge,
 accounting  byte and bits-per-element accounting of the compressed cache
 rtn         per-token asymmetric round-to-nearest key quantization (control):
             quantizer, record layout and decode attention
+kv          PGKQ-KV: values coded by the key encoder without the transform,
+            their reconstruction and decode attention
 
 Parity pins live in ``tests/test_oracle_pins.py``.  Parity unpinned: the
 absolute codebook values and the code values for any given input (the pages
@@ -28,5 +30,5 @@ print neither a codebook table nor a worked example); they are fixed only by the
 readings stated in each module plus the invariants the tests check.
 """
 
-from . import accounting, attn, calibrate, codebook, encode, layout, rht, rtn  # noqa: F401
+from . import accounting, attn, calibrate, codebook, encode, kv, layout, rht, rtn  # noqa: F401
 from .encode import Params  # noqa: F401

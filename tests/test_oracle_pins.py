@@ -615,3 +615,92 @@ def test_rtn_logits_converge_to_exact_with_bits():
     assert errs[0] > errs[1] > errs[2] > errs[3]
     assert 1.5 < errs[0] / errs[1] < 2.8
     assert 10 < errs[1] / errs[3] < 24
+
+
+# ------------------------------------------------------------------ PGKQ-KV (values coded)
+
+def test_kv_grid_values_reconstruct_exactly():
+    """Without the transform, a value whose pairs sit on (level_j, centre_a) points
+    reconstructs exactly: codes (j, a), residual 0, nu 0, QJL term 0."""
+    from oracle import kv
+    d, bm = 16, 3
+    pv = kv.value_params(d, bm, d)
+    c, t = codebook.lloyd_max_beta(d, bm)
+    lv, th = codebook.scaled_table(c, t, 2.0, d)
+    cen = encode.angle_centers(pv.b_angle)
+    rng = np.random.default_rng(4)
+    js = rng.integers(0, 1 << bm, size=(5, d // 2))
+    ac = rng.integers(0, 1 << pv.b_angle, size=(5, d // 2))
+    lv64 = lv.astype(np.float64)
+    V = np.zeros((5, d))
+    V[:, 0::2] = lv64[js] * np.cos(cen[ac])
+    V[:, 1::2] = lv64[js] * np.sin(cen[ac])
+    S = rng.standard_normal((d, d)).astype(np.float32)
+    f = kv.encode_values(V, lv, th, S, pv)
+    assert np.array_equal(f.rc, js) and np.array_equal(f.ac, ac)
+    assert np.all(f.nu == 0)
+    np.testing.assert_allclose(kv.dequantize_values(f, lv, S, pv), V, rtol=0, atol=1e-12)
+
+
+def test_kv_code_domain_output_equals_explicit_reconstruction():
+    """The decoder's form (weighted pair reconstructions, then one S^T product of
+    the weighted signed norms) equals p @ V-hat."""
+    from oracle import kv
+    rng = np.random.default_rng(8)
+    for d, bm, m in ((16, 2, 16), (64, 3, 64), (128, 4, 128), (64, 3, 0)):
+        pv = kv.value_params(d, bm, m)
+        V = rng.standard_normal((40, d)) * np.exp(0.5 * rng.standard_normal(d))
+        tab = kv.value_tables(V[None, None], bm)[0]
+        S = rng.standard_normal((m, d)).astype(np.float32) if m else None
+        f = kv.encode_values(V, tab[0], tab[1], S, pv)
+        p = rng.dirichlet(np.ones(40))
+        want = p @ kv.dequantize_values(f, tab[0], S, pv)
+        np.testing.assert_allclose(kv.code_domain_output(p, f, tab[0], S, pv), want,
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_kv_qjl_residual_estimate_is_unbiased():
+    """Over independent Gaussian projections, kappa ||eps|| S^T sign(S eps) has mean
+    eps (each coordinate within 4 standard errors) and per-coordinate variance
+    (pi/2) ||eps||^2 / m - eps_c^2 / m (the closed form of the vector estimator)."""
+    from oracle import attn as A
+    rng = np.random.default_rng(21)
+    d = m = 16
+    eps = rng.standard_normal(d)
+    R = 40000
+    S = rng.standard_normal((R, m, d))
+    u = np.einsum("rmd,d->rm", S, eps)
+    est = A.kappa(m) * np.linalg.norm(eps) * np.einsum("rm,rmd->rd", np.where(u >= 0, 1.0, -1.0), S)
+    mean = est.mean(axis=0)
+    var_cf = (math.pi / 2) * (eps @ eps) / m - eps ** 2 / m
+    se = np.sqrt(var_cf / R)
+    assert np.all(np.abs(mean - eps) <= 4 * se)
+    np.testing.assert_allclose(est.var(axis=0), var_cf, rtol=0.05)
+
+
+def test_kv_decode_error_shrinks_with_bits():
+    """PGKQ-KV output error against exact attention falls from b = 2 to 4 (values
+    coded; keys coded with the same bit width)."""
+    from oracle import kv
+    rng = np.random.default_rng(30)
+    d, T = 64, 256
+    K = rng.standard_normal((1, 1, T, d)) * np.exp(0.5 * rng.standard_normal(d))
+    V = rng.standard_normal((1, 1, T, d))
+    q = rng.standard_normal((1, 1, d))
+    signs = np.where(rng.integers(0, 2, (1, d)) > 0, 1.0, -1.0)
+    Sk = rng.standard_normal((1, d, d)).astype(np.float32)
+    Sv = rng.standard_normal((1, d, d)).astype(np.float32)
+    p_exact = attn.softmax_weights(K[0, 0] @ q[0, 0], 1 / math.sqrt(d))
+    exact = p_exact @ V[0, 0]
+    errs = []
+    for bm in (2, 3, 4):
+        pk = Params(d, bm, bm - 1, d)
+        pv = kv.value_params(d, bm, d)
+        c, t = codebook.lloyd_max_beta(d, bm)
+        kt = [codebook.scaled_table(c, t, calibrate.head_scale(calibrate.channel_sumsq(K[0, 0]), T), d)]
+        vt = kv.value_tables(V, bm)
+        kf = [[encode.encode_keys(K[0, 0], signs[0], None, kt[0][0], kt[0][1], Sk[0], pk)]]
+        vf = [[kv.encode_values(V[0, 0], vt[0][0], vt[0][1], Sv[0], pv)]]
+        out, _ = kv.decode_kv(q, kf, vf, kt, vt, Sk, Sv, signs, None, pk, pv)
+        errs.append(np.abs(out[0, 0] - exact).max())
+    assert errs[0] > errs[1] > errs[2]
