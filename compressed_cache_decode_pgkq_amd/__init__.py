@@ -19,6 +19,8 @@ from .api import (  # noqa: F401
     pgkq_estimate_logits,
     pgkq_fp16_decode_attn,
     pgkq_fp16_decode_workspace_bytes,
+    pgkq_kv_decode_attn,
+    pgkq_kv_decode_workspace_bytes,
     pgkq_lloyd_max_beta,
     pgkq_record_bytes,
     pgkq_rtn_decode_attn,

@@ -75,6 +75,10 @@ SIGNATURES = {
     "pgkq_fp16_decode_workspace_bytes": (_sz, [_i32, _i64, _i64, _i64, _i64, _O]),
     "pgkq_fp16_decode_attn": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _i32,
                                              _vp, _vp, _vp, _f32, _O, _vp, _sz, _vp]),
+    "pgkq_kv_decode_workspace_bytes": (_sz, [_P, _P, _i64, _i64, _i64, _i64, _O]),
+    "pgkq_kv_decode_attn": (ctypes.c_int, [_P, _P, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                           _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _O,
+                                           _vp, _sz, _vp]),
     "pgkq_rtn_record_bytes": (_sz, [_i32, _i32]),
     "pgkq_rtn_encode": (ctypes.c_int, [_i32, _i32, _vp, ctypes.c_int, _i64, _i64, _i64, _vp, _i64,
                                        _i64, _vp]),

@@ -228,6 +228,39 @@ def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor,
     return out
 
 
+# ---------------------------------------------------------------- PGKQ-KV
+
+
+def pgkq_kv_decode_workspace_bytes(pk: PgkqParams, pv: PgkqParams, n_seq, n_q, n_kv, n_tokens,
+                                   n_splits=0) -> int:
+    o = _opts(n_splits, None)
+    return int(L.lib().pgkq_kv_decode_workspace_bytes(ctypes.byref(pk.c()), ctypes.byref(pv.c()),
+                                                       n_seq, n_q, n_kv, n_tokens, ctypes.byref(o)))
+
+
+def pgkq_kv_decode_attn(pk: PgkqParams, pv: PgkqParams, q: torch.Tensor, codes_k: torch.Tensor,
+                        codes_v: torch.Tensor, n_kv: int, capacity: int, signs, perm, codebook_k,
+                        S_k, codebook_v, S_v, n_tokens=None, softmax_scale: float = 0.0,
+                        n_splits: int = 0, out=None, workspace=None, events=None, stream=None):
+    """Decode attention over key codes and value codes [n_seq, n_kv, capacity * record]."""
+    n_seq, n_q, d = q.shape
+    n_tok = capacity if n_tokens is None else int(n_tokens)
+    o = _opts(n_splits, events)
+    if out is None:
+        out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    ck, cv = pk.c(), pv.c()
+    nb = int(L.lib().pgkq_kv_decode_workspace_bytes(ctypes.byref(ck), ctypes.byref(cv), n_seq, n_q,
+                                                     n_kv, n_tok, ctypes.byref(o)))
+    ws, wsb = _ws(nb, q.device, workspace)
+    st = L.lib().pgkq_kv_decode_attn(ctypes.byref(ck), ctypes.byref(cv), _ptr(q), _dtype(q), n_seq,
+                                     n_q, n_kv, n_tok, capacity, _ptr(signs), _ptr(perm),
+                                     _ptr(codebook_k), _ptr(S_k), _ptr(codes_k), _ptr(codebook_v),
+                                     _ptr(S_v), _ptr(codes_v), _ptr(out), float(softmax_scale),
+                                     ctypes.byref(o), _ptr(ws), wsb, _stream(stream))
+    L.check(st, "pgkq_kv_decode_attn")
+    return out
+
+
 # ---------------------------------------------------------------- RTN control
 
 

@@ -1,0 +1,194 @@
+// Online softmax and the weighted sum of PGKQ-coded values (PGKQ-KV: the value
+// cache coded by the key encoder without the transform; EdgeLLM-Nano paper
+// page, PGKQ-KV paragraphs).
+//
+// The output sum_t p_t V-hat_t is accumulated in the code domain:
+//   * pair part: lane = 8 channels (4 pairs) of a token row, as for fp16
+//     values; each pair's joint code indexes a 2^P-entry LDS table of
+//     (level[rc] cos thetahat[ac], level[rc] sin thetahat[ac]) and is weighted
+//     by p_t;
+//   * QJL part: the same lane owns 8 sketch bits; it accumulates
+//     sum_t p_t nu_t bit_tj and sum_t p_t nu_t, giving
+//     a_j = sum_t p_t nu_t (2 bit_tj - 1).  The product kappa S^T a, linear in
+//     the partial states, is left to the merge kernel (one matrix-vector
+//     product per query head instead of one per partition).
+// The chunk's code words arrive lane = token (coalesced dword loads) and are
+// transposed through a wave-private LDS block.  Every wavefront writes its own
+// partial state (m, l, o[d], a[m]).
+#pragma once
+
+#include "softmax_pv.hpp"
+
+namespace pgkq {
+
+template <int D, int G, int WAVES, int BMV, bool QJLV>
+struct CodedPV {
+  static constexpr int N = D / 2;
+  static constexpr int P = 2 * BMV - 1;        // b_main + b_angle of the values
+  static constexpr int NCODES = 1 << P;
+  static constexpr int M = QJLV ? D : 0;
+  static constexpr int NC = N * P / 32;        // code words per token
+  static constexpr int NW = NC + M / 32;       // words per token
+  static constexpr int NROW = NW + (QJLV ? 1 : 0);  // LDS rows per chunk: words, norms
+  static constexpr int LPT = D / 8;            // lanes per token row
+  static constexpr int TPI = kWave / LPT;      // rows per pass
+  static constexpr int NIT = kWave / TPI;      // passes per chunk
+  static constexpr int WIDTH = 2 * D + 4;      // partial row: m, l, -, -, o[D], a[D]
+  static constexpr int LDS_WORDS = NROW * kWave;
+  static_assert(4 * P <= 32, "a lane's four pair codes span at most two words");
+
+  float m_run[G], l_lane[G], o[G][8], acc[G][8], spn[G];
+  int lane, wave, slot, dblk;
+  uint32_t row_bytes, nu_off;
+
+  struct VChunk {
+    uint32_t w[NW];
+    uint32_t nu;
+  };
+
+  __device__ __forceinline__ void init(int tid, int64_t capacity) {
+    lane = tid & 63;
+    wave = tid >> 6;
+    slot = lane / LPT;
+    dblk = lane % LPT;
+    row_bytes = 4u * static_cast<uint32_t>(capacity);
+    nu_off = NW * row_bytes;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m_run[g] = -INFINITY;
+      l_lane[g] = 0.f;
+      spn[g] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        o[g][k] = 0.f;
+        acc[g][k] = 0.f;
+      }
+    }
+  }
+
+  // code words of token c0 + lane (the whole stream is the buffer range;
+  // tokens past the split are masked when accumulated)
+  __device__ __forceinline__ void load_v(VChunk& vc, int64_t c0, __amdgpu_buffer_rsrc_t vr) const {
+    const uint32_t t4 = static_cast<uint32_t>(c0 + lane) * 4u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) vc.w[w] = buf_load_b32(vr, t4 + w * row_bytes);
+    if constexpr (QJLV) vc.nu = buf_load_b16(vr, nu_off + t4 / 2);
+  }
+
+  // s: raw scores of token c0 + lane; p_rows: the wavefront's [64][G] weights;
+  // vw: its LDS_WORDS transposition block; vtab: the pair table; rows at or
+  // beyond c_end carry no weight.
+  __device__ __forceinline__ void chunk(const float (&s)[G], bool valid, float scale_log2,
+                                        const VChunk& vc, float* p_rows, uint32_t* vw,
+                                        const float2* vtab, int64_t c0, int64_t c_end) {
+    float pv[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float z = valid ? s[g] * scale_log2 : -INFINITY;
+      const float mnew = fmaxf(m_run[g], wave_max_uniform(z));
+      if (mnew > m_run[g]) {  // wave-uniform
+        const float alpha = fast_exp2(m_run[g] - mnew);
+        l_lane[g] *= alpha;
+        spn[g] *= alpha;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          o[g][k] *= alpha;
+          acc[g][k] *= alpha;
+        }
+        m_run[g] = mnew;
+      }
+      pv[g] = valid ? fast_exp2(z - m_run[g]) : 0.f;
+      l_lane[g] += pv[g];
+    }
+    if constexpr (G == 1) {
+      p_rows[lane] = pv[0];
+    } else if constexpr (G == 2) {
+      *reinterpret_cast<float2*>(p_rows + lane * 2) = make_float2(pv[0], pv[1]);
+    } else {
+#pragma unroll
+      for (int g = 0; g < G; g += 4)
+        *reinterpret_cast<float4*>(p_rows + lane * G + g) = make_float4(pv[g], pv[g + 1], pv[g + 2], pv[g + 3]);
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) vw[w * kWave + lane] = vc.w[w];
+    if constexpr (QJLV) vw[NW * kWave + lane] = vc.nu;
+    wave_lds_sync();
+
+    const int o0 = 4 * P * dblk;  // first polar bit of this lane's pairs
+    const int w0 = o0 >> 5, sh = o0 & 31;
+    const int w1 = w0 + 1 < NROW ? w0 + 1 : NROW - 1;
+    constexpr uint32_t mask = (1u << P) - 1u;
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      if ((it & 3) == 0) sched_fence();
+      const int r = it * TPI + slot;
+      float pp[G];
+      lds_fetch<G>(p_rows + r * G, pp);
+      const uint64_t bits = uint64_t(vw[w0 * kWave + r]) | (uint64_t(vw[w1 * kWave + r]) << 32);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t code = static_cast<uint32_t>(bits >> (sh + P * j)) & mask;
+        const float2 t = vtab[code];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          o[g][2 * j] = fmaf(pp[g], t.x, o[g][2 * j]);
+          o[g][2 * j + 1] = fmaf(pp[g], t.y, o[g][2 * j + 1]);
+        }
+      }
+      if constexpr (QJLV) {
+        const uint32_t sb = (vw[(NC + (dblk >> 2)) * kWave + r] >> (8 * (dblk & 3))) & 0xFFu;
+        const float nu = half_bits_to_float(static_cast<uint16_t>(vw[NW * kWave + r]));
+        const bool live = c0 + r < c_end;  // a slot past the cache may hold any bits
+        float fb[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) fb[k] = static_cast<float>((sb >> k) & 1u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pn = live ? pp[g] * nu : 0.f;
+          spn[g] += pn;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(fb[k], pn, acc[g][k]);
+        }
+      }
+    }
+    wave_lds_sync();
+  }
+
+  // Partial state of this wavefront as partial `pidx` of `n_parts` for query
+  // heads row0 .. row0 + G - 1.
+  __device__ __forceinline__ void finish_wave(float* __restrict__ partial, size_t row0, int pidx,
+                                              int n_parts) {
+#pragma unroll
+    for (int off = LPT; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        spn[g] += __shfl_xor(spn[g], off, kWave);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          o[g][k] += __shfl_xor(o[g][k], off, kWave);
+          acc[g][k] += __shfl_xor(acc[g][k], off, kWave);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float l_w = wave_sum(l_lane[g]);
+      float* part = partial + ((row0 + g) * n_parts + pidx) * WIDTH;
+      if (lane < LPT) {
+        *reinterpret_cast<float4*>(part + 4 + dblk * 8) = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
+        *reinterpret_cast<float4*>(part + 8 + dblk * 8) = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
+        float a[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = QJLV ? 2.f * acc[g][k] - spn[g] : 0.f;
+        *reinterpret_cast<float4*>(part + 4 + D + dblk * 8) = make_float4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<float4*>(part + 8 + D + dblk * 8) = make_float4(a[4], a[5], a[6], a[7]);
+      }
+      if (lane == 0) {
+        part[0] = m_run[g];
+        part[1] = l_w;
+      }
+    }
+  }
+};
+
+}  // namespace pgkq

@@ -21,25 +21,11 @@
 //                softmax per wavefront, then lane = 8 channels of a token for
 //                the P.V accumulation (16-byte fp16 V loads, fp32 accumulate);
 //   merge        log-sum-exp merge of the split partial states.
-#include "softmax_pv.hpp"
+#include "scan.hpp"
 
 namespace pgkq {
 
 namespace {
-
-constexpr int kScanThreads = 256;
-constexpr int kScanWaves = kScanThreads / kWave;
-// waves per SIMD the register allocator must leave room for
-#ifndef PGKQ_SCAN_MIN_WAVES
-#define PGKQ_SCAN_MIN_WAVES 2
-#endif
-constexpr int kScanMinWavesPerEU = PGKQ_SCAN_MIN_WAVES;
-// table lookups issued per scheduling group of the score loop
-#ifndef PGKQ_PAIR_GROUP
-#define PGKQ_PAIR_GROUP 8
-#endif
-constexpr int kPairGroup = PGKQ_PAIR_GROUP;
-
 
 // ------------------------------------------------------------------ append
 
@@ -213,214 +199,6 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
       double acc = 0.0;
       for (int c = 0; c < D; ++c) acc += double(Sr[c]) * sq64[c];
       out[pl.off_sq() + r] = static_cast<float>(acc);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ scan
-
-template <int D, int BM, int G>
-struct ScanShape {
-  static constexpr int N = D / 2;
-  static constexpr int BA = BM - 1;
-  static constexpr int P = BM + BA;
-  static constexpr int L = 1 << BM;
-  static constexpr int A = 1 << BA;
-  static constexpr int NCODES = 1 << P;
-  static constexpr bool JOINT = N * NCODES * G <= 8192;  // <= 32 KiB of LDS
-  static constexpr int TABLE_FLOATS = JOINT ? N * NCODES * G : N * A * G + L;
-};
-
-template <int P>
-__device__ __forceinline__ uint32_t code_at(const uint32_t* cw, int i) {
-  const int off = P * i;
-  const int w = off >> 5, s = off & 31;
-  constexpr uint32_t mask = (1u << P) - 1u;
-  if (s + P <= 32) return (cw[w] >> s) & mask;
-  return __builtin_amdgcn_alignbit(cw[w + 1], cw[w], s) & mask;
-}
-
-template <int D, int BM, bool QJL, int G, bool LOGITS>
-__global__ void __launch_bounds__(kScanThreads, kScanMinWavesPerEU)
-decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half* __restrict__ V) {
-  using SS = ScanShape<D, BM, G>;
-  constexpr int N = SS::N, BA = SS::BA, P = SS::P, L = SS::L, A = SS::A, NCODES = SS::NCODES;
-  constexpr bool JOINT = SS::JOINT;
-  constexpr int M = QJL ? D : 0;
-  constexpr int NC = N * P / 32;
-  constexpr int NW = NC + M / 32;
-  constexpr int NQT = QJL ? (M / 4) * 16 * G : 1;
-  constexpr int MERGE_FLOATS = SoftmaxPV<D, G, kScanWaves>::MERGE_FLOATS;
-  constexpr int MAIN_FLOATS = SS::TABLE_FLOATS > MERGE_FLOATS ? SS::TABLE_FLOATS : MERGE_FLOATS;
-  (void)BA;
-
-  __shared__ __align__(16) float s_tab[MAIN_FLOATS];
-  __shared__ __align__(16) float s_qt[NQT];
-  __shared__ __align__(16) float s_p[kScanWaves][kWave][G];
-
-  const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t b = blockIdx.z;
-  const PrepLayout pl{D, N, A, M};
-  const float* lv = a.codebook + size_t(h) * 2 * L;
-  const float* prep0 = a.prep + (size_t(b) * a.n_q + size_t(h) * G) * pl.stride();
-
-  const int64_t t_begin = int64_t(split) * a.tokens_per_split;
-  const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
-  const int64_t stream = b * a.n_kv + h;
-  const uint8_t* cbase = codes + size_t(stream) * a.stream_bytes;
-  // buffer ranges: the whole code stream, and this stream's V rows [0, t_end)
-  const __amdgpu_buffer_rsrc_t crs = make_rsrc(cbase, static_cast<uint32_t>(a.stream_bytes));
-  const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
-  const uint32_t nu_off = 4u * NW * static_cast<uint32_t>(a.capacity);
-  const uint32_t row_bytes = 4u * static_cast<uint32_t>(a.capacity);
-
-  SoftmaxPV<D, G, kScanWaves> sm;
-  sm.init(tid);
-  const int lane = sm.lane, wave = sm.wave;
-
-  // Per chunk of 64 tokens, every load of the chunk (code words, norms, V rows)
-  // is issued at its start; V is consumed only after the score, so its latency
-  // hides behind the table lookups.
-  uint32_t cw[NW];
-  float nu = 0.f;
-  typename SoftmaxPV<D, G, kScanWaves>::VChunk vc;
-  // lanes past the split end read neighbouring (or, past the stream, zero)
-  // words; their scores are masked
-  auto load_codes = [&](int64_t c) {
-    const uint32_t t4 = static_cast<uint32_t>(c + lane) * 4u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) cw[w] = buf_load_b32(crs, t4 + w * row_bytes);
-    if constexpr (QJL) nu = half_bits_to_float(buf_load_b16(crs, nu_off + t4 / 2));
-  };
-
-  // ---- tables: one thread per (pair, query head)
-  {
-    float lvr[L];
-#pragma unroll
-    for (int r = 0; r < L; ++r) lvr[r] = lv[r];
-    for (int ig = tid; ig < N * G; ig += kScanThreads) {
-      const int i = ig / G, g = ig % G;
-      const float* lut = prep0 + size_t(g) * pl.stride() + pl.off_lut() + i * A;
-      float lt[A];
-#pragma unroll
-      for (int ac = 0; ac < A; ++ac) lt[ac] = lut[ac];
-      if constexpr (JOINT) {
-#pragma unroll
-        for (int code = 0; code < NCODES; ++code)
-          s_tab[(i * NCODES + code) * G + g] = lvr[code & (L - 1)] * lt[code >> BM];
-      } else {
-#pragma unroll
-        for (int ac = 0; ac < A; ++ac) s_tab[(i * A + ac) * G + g] = lt[ac];
-      }
-    }
-    if constexpr (!JOINT) {
-      if (tid < L) s_tab[N * A * G + tid] = lvr[tid];
-    }
-  }
-  if constexpr (QJL) {
-    const float kappa = 1.2533141373155003f / float(M);  // sqrt(pi/2) / m
-    for (int kg = tid; kg < (M / 4) * G; kg += kScanThreads) {
-      const int k = kg / G, g = kg % G;
-      const float* sq = prep0 + size_t(g) * pl.stride() + pl.off_sq() + 4 * k;
-      const float q0 = sq[0], q1 = sq[1], q2 = sq[2], q3 = sq[3];
-#pragma unroll
-      for (int nib = 0; nib < 16; ++nib) {
-        const float v = ((nib & 1) ? q0 : -q0) + ((nib & 2) ? q1 : -q1) + ((nib & 4) ? q2 : -q2) +
-                        ((nib & 8) ? q3 : -q3);
-        s_qt[(k * 16 + nib) * G + g] = kappa * v;
-      }
-    }
-  }
-  __syncthreads();
-
-  // Token ranges: either the workgroup's split is shared by its wavefronts in
-  // interleaved chunks, or (wave_parts) every wavefront scans a contiguous
-  // partition of its own and writes its own partial state.
-  int64_t c_first, c_end, c_step;
-  if (a.wave_parts) {
-    const int64_t tpw = a.tokens_per_split / kScanWaves;
-    c_first = t_begin + int64_t(wave) * tpw;
-    c_end = min<int64_t>(c_first + tpw, t_end);
-    c_step = kWave;
-  } else {
-    c_first = t_begin + int64_t(wave) * kWave;
-    c_end = t_end;
-    c_step = kScanThreads;
-  }
-  for (int64_t c0 = c_first; c0 < c_end; c0 += c_step) {
-    const int64_t t = c0 + lane;
-    const bool valid = t < c_end;
-    load_codes(c0);
-    if constexpr (!LOGITS) sm.load_v(vc, c0, vrs);
-
-    float s[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) s[g] = 0.f;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      // bound the work in flight (registers): the code words of each group of
-      // 8 pairs are pinned at the group's start, so neither their bit-field
-      // extracts nor their table reads are hoisted above it
-      if ((i % kPairGroup) == 0) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) pin_reg(s[g]);
-#pragma unroll
-        for (int w = (P * i) / 32; w <= (P * (i + kPairGroup) - 1) / 32 && w < NC; ++w) pin_reg(cw[w]);
-      }
-      const uint32_t code = code_at<P>(cw, i);
-      float e[G];
-      if constexpr (JOINT) {
-        lds_fetch<G>(&s_tab[(i * NCODES + code) * G], e);
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[g] += e[g];
-      } else {
-        const float lvl = s_tab[N * A * G + (code & (L - 1))];
-        lds_fetch<G>(&s_tab[(i * A + (code >> BM)) * G], e);
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[g] = fmaf(lvl, e[g], s[g]);
-      }
-    }
-    if constexpr (QJL) {
-      float qs[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) qs[g] = 0.f;
-#pragma unroll
-      for (int k = 0; k < M / 4; ++k) {
-        if ((k % kPairGroup) == 0) {
-#pragma unroll
-          for (int g = 0; g < G; ++g) pin_reg(qs[g]);
-          pin_reg(cw[NC + (k >> 3)]);
-        }
-        const uint32_t nib = (cw[NC + (k >> 3)] >> (4 * (k & 7))) & 15u;
-        float e[G];
-        lds_fetch<G>(&s_qt[(k * 16 + nib) * G], e);
-#pragma unroll
-        for (int g = 0; g < G; ++g) qs[g] += e[g];
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = fmaf(nu, qs[g], s[g]);
-    }
-
-    if constexpr (LOGITS) {
-      if (valid) {
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          a.logits[(size_t(b) * a.n_q + size_t(h) * G + g) * a.n_tokens + t] = s[g];
-      }
-    } else {
-      sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0]);
-    }
-  }
-  if constexpr (!LOGITS) {
-    const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
-    if (a.wave_parts) {
-      sm.finish_wave(a.partial, row0, split * kScanWaves + wave, a.n_splits * kScanWaves);
-    } else {
-      __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
-      sm.finish(s_tab, tid, a.n_splits, split, a.out, a.partial, row0);
     }
   }
 }

@@ -520,6 +520,115 @@ pgkq_status pgkq_decode_step(const pgkq_params* p, const void* q, pgkq_dtype q_d
                        workspace_bytes, stream, &step);
 }
 
+// ---------------------------------------------------------------- PGKQ-KV
+
+static pgkq_status check_kv(const pgkq_params* pk, const pgkq_params* pv, Geometry* gk,
+                            Geometry* gv) {
+  pgkq_status st = check_params(pk, gk);
+  if (st != PGKQ_OK) return st;
+  if ((st = check_params(pv, gv)) != PGKQ_OK) return st;
+  if (gv->d != gk->d || gv->hadamard != 0) return PGKQ_ERR_UNSUPPORTED;
+  if ((gv->m != 0) != (gk->m != 0)) return PGKQ_ERR_UNSUPPORTED;
+  const int k = gk->bm, v = gv->bm;
+  const bool pair_ok = (k == v) || (v == 2 && (k == 3 || k == 4));
+  return pair_ok ? PGKQ_OK : PGKQ_ERR_UNSUPPORTED;
+}
+
+static size_t kv_ws(const Geometry& gk, int64_t n_seq, int64_t n_q, const Splits& sp) {
+  const pgkq::PrepLayout pl{gk.d, gk.n(), 1 << gk.ba, gk.m};
+  return round_up(size_t(n_seq) * n_q * pl.stride() * sizeof(float), 256) +
+         round_up(size_t(n_seq) * n_q * 4 * sp.n * (2 * gk.d + 4) * sizeof(float), 256);
+}
+
+size_t pgkq_kv_decode_workspace_bytes(const pgkq_params* pk, const pgkq_params* pv, int64_t n_seq,
+                                      int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                      const pgkq_launch_opts* opts) {
+  Geometry gk, gv;
+  if (check_kv(pk, pv, &gk, &gv) != PGKQ_OK || n_seq < 1 || n_q < 1 || n_kv < 1 || n_tokens < 0)
+    return 0;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  return kv_ws(gk, n_seq, n_q, sp);
+}
+
+pgkq_status pgkq_kv_decode_attn(const pgkq_params* pk, const pgkq_params* pv, const void* q,
+                                pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q, int64_t n_kv,
+                                int64_t n_tokens, int64_t capacity, const int8_t* signs,
+                                const uint16_t* perm, const float* codebook_k, const float* S_k,
+                                const void* codes_k, const float* codebook_v, const float* S_v,
+                                const void* codes_v, float* out, float softmax_scale,
+                                const pgkq_launch_opts* opts, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Geometry g, gv;
+  pgkq_status st = check_kv(pk, pv, &g, &gv);
+  if (st != PGKQ_OK) return st;
+  if (!q || !signs || !codebook_k || !codes_k || !codebook_v || !codes_v || !out || !workspace)
+    return PGKQ_ERR_NULL;
+  if (g.m && (!S_k || !S_v)) return PGKQ_ERR_NULL;
+  if ((st = check_dtype(q_dtype, true)) != PGKQ_OK) return st;
+  if ((st = check_streams(n_seq, n_kv)) != PGKQ_OK) return st;
+  int group = 0;
+  if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
+  if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;
+  if (!fits_buffer(capacity, std::max(g.record_bytes(), gv.record_bytes()), 0))
+    return PGKQ_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(signs) || !aligned16(codebook_k) || !aligned16(codes_k) ||
+      !aligned16(codebook_v) || !aligned16(codes_v) || !aligned16(out) || !aligned16(workspace) ||
+      (perm && !aligned16(perm)) || (S_k && !aligned16(S_k)) || (S_v && !aligned16(S_v)))
+    return PGKQ_ERR_ALIGN;
+  const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
+                                  opts ? opts->n_splits : 0);
+  if (workspace_bytes < kv_ws(g, n_seq, n_q, sp)) return PGKQ_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_tokens == 0) return map_hip(zero_fill(out, size_t(n_seq) * n_q * g.d, s));
+  const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
+  pgkq::DecodeArgs a{};
+  a.q = q;
+  a.q_dtype = static_cast<int>(q_dtype);
+  a.hadamard = g.hadamard;
+  a.n_seq = n_seq;
+  a.n_q = n_q;
+  a.n_kv = n_kv;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.group = group;
+  a.signs = signs;
+  a.perm = perm;
+  a.codebook = codebook_k;
+  a.S = g.m ? S_k : nullptr;
+  a.codes = static_cast<const uint8_t*>(codes_k);
+  a.stream_bytes = size_t(capacity) * g.record_bytes();
+  a.out = out;
+  a.prep = static_cast<float*>(workspace);
+  a.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       round_up(size_t(n_seq) * n_q * pl.stride() * 4, 256));
+  a.n_splits = sp.n;
+  a.tokens_per_split = sp.tokens_per;
+  a.wave_parts = sp.wave_parts;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(g.d));
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.append_slot = -1;
+  a.bm_v = gv.bm;
+  a.codes_v = static_cast<const uint8_t*>(codes_v);
+  a.stream_bytes_v = size_t(capacity) * gv.record_bytes();
+  a.codebook_v = codebook_v;
+  a.S_v = gv.m ? S_v : nullptr;
+  hipError_t e = pgkq::launch_query_prep(g, a, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_start) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  e = pgkq::launch_kv_decode_scan(g, a, s);
+  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  if (opts && opts->scan_stop) {
+    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+      return PGKQ_ERR_HIP;
+  }
+  return map_hip(pgkq::launch_kv_merge(a, g.d, 4 * sp.n, s));
+}
+
 pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
                                  int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
                                  int64_t capacity, const int8_t* signs, const uint16_t* perm,

@@ -94,6 +94,12 @@ struct DecodeArgs {
   const __half* v_new;
   uint8_t* codes_w;
   __half* V_w;
+  // PGKQ-KV: values coded by the key encoder without the transform
+  int bm_v;                 // 0: fp16 values in V
+  const uint8_t* codes_v;
+  size_t stream_bytes_v;
+  const float* codebook_v;  // [n_kv][2 L_v]
+  const float* S_v;         // [n_kv][d][d] or null
 };
 
 struct Fp16DecodeArgs {
@@ -150,6 +156,8 @@ hipError_t launch_encode(const Geometry& g, const EncodeArgs& a, hipStream_t s);
 hipError_t launch_query_prep(const Geometry& g, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_scan(const Geometry& g, const DecodeArgs& a, bool logits_mode,
                               hipStream_t s);
+hipError_t launch_kv_decode_scan(const Geometry& g, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_kv_merge(const DecodeArgs& a, int d, int n_parts, hipStream_t s);
 hipError_t launch_partial_merge(int d, int64_t n_seq, int64_t n_q, int n_splits,
                                 const float* partial, float* out, hipStream_t s);
 hipError_t launch_fp16_decode(const Fp16DecodeArgs& a, hipStream_t s);

@@ -210,6 +210,41 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * PGKQ-KV: values coded as well (EdgeLLM-Nano paper page, PGKQ-KV paragraphs:
+ * PGKQ's polar codes, Lloyd-Max tables and QJL sketch applied to V, with the
+ * Hadamard rotation disabled for V).
+ *
+ * The value cache is encoded with pgkq_encode itself, called on V with value
+ * parameters pv (pv->hadamard = 0; signs are then ignored and perm must be
+ * NULL) and the value table and projection (pgkq_calibrate on V gives the
+ * table).  Its records have the key layout above.  The decoder forms
+ * sum_t p_t V-hat_t with V-hat_t the reconstruction the codes define: per pair
+ * level_v[rc] (cos thetahat[ac], sin thetahat[ac]), plus, with QJL,
+ * sqrt(pi/2)/m * nu_t * S_v^T (2 bits_t - 1).
+ * Supported (b_main of K, b_main of V): equal widths 2, 3, 4, or V at 2 with
+ * K at 3 or 4; QJL on both or on neither; same head_dim.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of workspace pgkq_kv_decode_attn needs (0 if the parameters are invalid). */
+size_t pgkq_kv_decode_workspace_bytes(const pgkq_params* pk, const pgkq_params* pv, int64_t n_seq,
+                                      int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                      const pgkq_launch_opts* opts);
+
+/* Decode attention over PGKQ key codes and PGKQ value codes:
+ *   q, signs, perm, codebook_k, S_k, codes_k as for pgkq_decode_attn;
+ *   codebook_v [n_kv][2 L_v] fp32, S_v [n_kv][d][d] fp32 (NULL without QJL),
+ *   codes_v written by pgkq_encode(pv, V, ...) with the same capacity;
+ *   out [n_seq][n_q][d] fp32. */
+pgkq_status pgkq_kv_decode_attn(const pgkq_params* pk, const pgkq_params* pv, const void* q,
+                                pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q, int64_t n_kv,
+                                int64_t n_tokens, int64_t capacity, const int8_t* signs,
+                                const uint16_t* perm, const float* codebook_k, const float* S_k,
+                                const void* codes_k, const float* codebook_v, const float* S_v,
+                                const void* codes_v, float* out, float softmax_scale,
+                                const pgkq_launch_opts* opts, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * RTN control: per-token asymmetric round-to-nearest keys (EdgeLLM-Nano paper
  * page, "Comparison to simpler baselines": K quantized per token to INT3 or
  * INT4 with an FP16 scale and zero-point per key vector, V in FP16).

@@ -3,9 +3,10 @@ larger GQA caches the PGKQ path is measured on.
 
 Recipe (identical for every consumer):
 
-* ``SeedSequence(20261010 + config_id)`` spawns seven children, in this order:
+* ``SeedSequence(20261010 + config_id)`` spawns eight children, in this order:
   channel scales, outlier channel indices, keys, queries, values, RHT signs,
-  QJL projection.  The key and value children each spawn one grandchild per
+  QJL projection, value QJL projection (the first seven are the same as when
+  seven were spawned).  The key and value children each spawn one grandchild per
   (sequence, kv-head) stream, so any stream can be regenerated on its own.
   Every child drives a ``numpy.random.Generator(PCG64(child))``.
 * channel scale[h, c] = exp(0.5 * N(0, 1)); ``n_outliers`` channels per kv-head,
@@ -14,7 +15,8 @@ Recipe (identical for every consumer):
 * q ~ N(0, 1), cast to the query dtype (fp32, or bf16 by round-to-nearest-even).
 * V ~ N(0, 1), cast to fp16.
 * RHT signs: Rademacher +-1 per (kv-head, channel), int8.
-* QJL projection S[h, j, c] ~ N(0, 1), cast to fp32, one m x d matrix per kv-head.
+* QJL projection S[h, j, c] ~ N(0, 1), cast to fp32, one m x d matrix per kv-head;
+  the value projection (for coded values) likewise, d x d.
 
 Only draws and dtype casts live here: nothing of the method's arithmetic.
 """
@@ -26,7 +28,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 BASE_SEED = 20261010
-_CHILDREN = ("scales", "outliers", "keys", "queries", "values", "signs", "proj")
+_CHILDREN = ("scales", "outliers", "keys", "queries", "values", "signs", "proj", "proj_v")
 
 
 @dataclass(frozen=True)
@@ -161,6 +163,13 @@ def projection(cfg: WorkloadConfig) -> np.ndarray:
     s = _rng(_children(cfg)["proj"]).standard_normal(
         (cfg.n_kv, cfg.proj_rows, cfg.head_dim), dtype=np.float32)
     return s
+
+
+def value_projection(cfg: WorkloadConfig) -> np.ndarray:
+    """A second Gaussian projection [n_kv, head_dim, head_dim] fp32, for the value
+    sketch when the values are coded as well."""
+    return _rng(_children(cfg)["proj_v"]).standard_normal(
+        (cfg.n_kv, cfg.head_dim, cfg.head_dim), dtype=np.float32)
 
 
 def make_inputs(cfg: WorkloadConfig, streams=None, with_values: bool = True) -> dict:
