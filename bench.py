@@ -35,7 +35,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_scan_gqa32k_b16_traffic.json")
-SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/decode.hip",
+SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/scan.hpp",
+                "compressed_cache_decode_pgkq_amd/csrc/pgkq_internal.hpp",
+                "compressed_cache_decode_pgkq_amd/csrc/coded_pv.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/softmax_pv.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
 
@@ -121,10 +123,11 @@ def measure_copy(torch, dev, reps: int = 10) -> float:
     return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
-def run_controls(api, torch, dev, cfg, K, V, q, flush, E, reps: int = 20):
-    """The same decode workload on the RTN INT4 / INT3 key caches and on the
-    uncompressed fp16 cache (same keys, values, queries and split count): scan
-    kernel time and its share of the HBM peak."""
+def run_controls(api, torch, dev, cfg, K, V, q, signs, S, flush, E, reps: int = 20):
+    """The same decode workload on the RTN INT4 / INT3 key caches, with PGKQ-coded
+    values as well (PGKQ-KV k3v3), and on the uncompressed fp16 cache (same
+    keys, values, queries and split count): scan kernel time and its share of
+    the HBM peak."""
     n_seq, n_kv, T, d = K.shape
     res = {}
     e0, e1 = E(), E()
@@ -155,6 +158,28 @@ def run_controls(api, torch, dev, cfg, K, V, q, flush, E, reps: int = 20):
                                  "scan_gbs": alg / (ms * 1e-3) / 1e9,
                                  "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del codes, ws
+    # PGKQ-KV k3v3: values coded too (key table and projection as in the main path)
+    from synth.inputs import value_projection
+    pk = api.PgkqParams(d, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
+    pv = api.PgkqParams(d, cfg.b_main, cfg.b_angle, cfg.qjl_m, 0)
+    Sv = torch.from_numpy(value_projection(cfg)).to(dev)
+    _, _, cbk = api.pgkq_calibrate(pk, K)
+    _, _, cbv = api.pgkq_calibrate(pv, V)
+    ck = api.pgkq_encode(pk, K, signs, None, cbk, S, capacity=T)
+    cv = api.pgkq_encode(pv, V, signs, None, cbv, Sv, capacity=T)
+    ws = torch.empty(api.pgkq_kv_decode_workspace_bytes(pk, pv, n_seq, cfg.n_q, n_kv, T, cfg.n_splits),
+                     dtype=torch.uint8, device=dev)
+    ms = timed(lambda: api.pgkq_kv_decode_attn(pk, pv, q, ck, cv, n_kv, T, signs, None, cbk, S, cbv,
+                                               Sv, n_splits=cfg.n_splits, out=out, workspace=ws,
+                                               events=(e0, e1)))
+    rbk, rbv = api.pgkq_record_bytes(pk), api.pgkq_record_bytes(pv)
+    alg = n_seq * n_kv * T * (rbk + rbv)
+    res["pgkq_kv_k3v3"] = {"record_bytes": rbk + rbv, "scan_ms": ms,
+                           "cache_tokens_per_s_scan": n_seq * T / (ms * 1e-3),
+                           "scan_gbs": alg / (ms * 1e-3) / 1e9,
+                           "frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "note": "VALU-bound: values decoded in the code domain"}
+    del ck, cv, ws
     ws = torch.empty(max(api.pgkq_fp16_decode_workspace_bytes(d, n_seq, cfg.n_q, n_kv, T, cfg.n_splits), 256),
                      dtype=torch.uint8, device=dev)
     ms = timed(lambda: api.pgkq_fp16_decode_attn(q, K, V, n_splits=cfg.n_splits, out=out, workspace=ws,
@@ -257,7 +282,7 @@ def main():
     pct = lambda k: {"p10": float(np.percentile(ph[:, k], 10)), "p50": float(np.median(ph[:, k])),  # noqa: E731
                      "p90": float(np.percentile(ph[:, k], 90))}
     copy_gbs = measure_copy(torch, dev)
-    controls = run_controls(api, torch, dev, cfg, K, V, q, flush, E)
+    controls = run_controls(api, torch, dev, cfg, K, V, q, signs, S, flush, E)
 
     token_heads = n_seq * n_kv * T
     alg_bytes = token_heads * (rb + 2 * d)

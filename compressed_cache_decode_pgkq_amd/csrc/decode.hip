@@ -194,11 +194,27 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
     out[pl.off_lut() + e] = static_cast<float>(sq64[2 * i] * cs + sq64[2 * i + 1] * sn);
   }
   if constexpr (QJL) {
-    for (int r = tid; r < M; r += blockDim.x) {
-      const float* Sr = S + (size_t(h) * M + r) * D;
+    // S_h q~: four adjacent threads per row of S, each reading one contiguous
+    // quarter of the row with 16-byte loads (a 128-byte line per thread at
+    // d = 128); float64 products, the quarters summed by DPP quad exchanges
+    constexpr int TPR = 4;
+    constexpr int CPT = D / TPR;
+    const int part = tid & (TPR - 1);
+    for (int r = tid / TPR; r < M; r += blockDim.x / TPR) {
+      const float4* Sr = reinterpret_cast<const float4*>(S + (size_t(h) * M + r) * D + part * CPT);
       double acc = 0.0;
-      for (int c = 0; c < D; ++c) acc += double(Sr[c]) * sq64[c];
-      out[pl.off_sq() + r] = static_cast<float>(acc);
+#pragma unroll
+      for (int k = 0; k < CPT / 4; ++k) {
+        const float4 v = Sr[k];
+        const int c = part * CPT + 4 * k;
+        acc = fma(double(v.x), sq64[c], acc);
+        acc = fma(double(v.y), sq64[c + 1], acc);
+        acc = fma(double(v.z), sq64[c + 2], acc);
+        acc = fma(double(v.w), sq64[c + 3], acc);
+      }
+      acc += quad_xor<1>(acc);
+      acc += quad_xor<2>(acc);
+      if (part == 0) out[pl.off_sq() + r] = static_cast<float>(acc);
     }
   }
 }

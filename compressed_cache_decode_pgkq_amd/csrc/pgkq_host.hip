@@ -109,6 +109,7 @@ Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested,
   return Splits{static_cast<int>(ns), tps, 0};
 }
 
+// Decode workspace: query prep | split partials, each region 256-byte aligned.
 size_t decode_ws(const Geometry& g, int64_t n_seq, int64_t n_q, const Splits& sp) {
   const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
   size_t bytes = round_up(size_t(n_seq) * n_q * pl.stride() * sizeof(float), 256);
