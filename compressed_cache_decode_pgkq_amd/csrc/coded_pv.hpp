@@ -34,7 +34,11 @@ struct CodedPV {
   static constexpr int TPI = kWave / LPT;      // rows per pass
   static constexpr int NIT = kWave / TPI;      // passes per chunk
   static constexpr int WIDTH = 2 * D + 4;      // partial row: m, l, -, -, o[D], a[D]
-  static constexpr int LDS_WORDS = NROW * kWave;
+  // transposition block rows are padded by one word: the lanes of a token row
+  // read different words of the same token, which would otherwise all fall in
+  // one LDS bank
+  static constexpr int VW_STRIDE = kWave + 1;
+  static constexpr int LDS_WORDS = NROW * VW_STRIDE;
   static_assert(4 * P <= 32, "a lane's four pair codes span at most two words");
 
   float m_run[G], l_lane[G], o[G][8], acc[G][8], spn[G];
@@ -110,8 +114,8 @@ struct CodedPV {
         *reinterpret_cast<float4*>(p_rows + lane * G + g) = make_float4(pv[g], pv[g + 1], pv[g + 2], pv[g + 3]);
     }
 #pragma unroll
-    for (int w = 0; w < NW; ++w) vw[w * kWave + lane] = vc.w[w];
-    if constexpr (QJLV) vw[NW * kWave + lane] = vc.nu;
+    for (int w = 0; w < NW; ++w) vw[w * VW_STRIDE + lane] = vc.w[w];
+    if constexpr (QJLV) vw[NW * VW_STRIDE + lane] = vc.nu;
     wave_lds_sync();
 
     const int o0 = 4 * P * dblk;  // first polar bit of this lane's pairs
@@ -124,7 +128,7 @@ struct CodedPV {
       const int r = it * TPI + slot;
       float pp[G];
       lds_fetch<G>(p_rows + r * G, pp);
-      const uint64_t bits = uint64_t(vw[w0 * kWave + r]) | (uint64_t(vw[w1 * kWave + r]) << 32);
+      const uint64_t bits = uint64_t(vw[w0 * VW_STRIDE + r]) | (uint64_t(vw[w1 * VW_STRIDE + r]) << 32);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t code = static_cast<uint32_t>(bits >> (sh + P * j)) & mask;
@@ -136,8 +140,8 @@ struct CodedPV {
         }
       }
       if constexpr (QJLV) {
-        const uint32_t sb = (vw[(NC + (dblk >> 2)) * kWave + r] >> (8 * (dblk & 3))) & 0xFFu;
-        const float nu = half_bits_to_float(static_cast<uint16_t>(vw[NW * kWave + r]));
+        const uint32_t sb = (vw[(NC + (dblk >> 2)) * VW_STRIDE + r] >> (8 * (dblk & 3))) & 0xFFu;
+        const float nu = half_bits_to_float(static_cast<uint16_t>(vw[NW * VW_STRIDE + r]));
         const bool live = c0 + r < c_end;  // a slot past the cache may hold any bits
         float fb[8];
 #pragma unroll
@@ -154,10 +158,8 @@ struct CodedPV {
     wave_lds_sync();
   }
 
-  // Partial state of this wavefront as partial `pidx` of `n_parts` for query
-  // heads row0 .. row0 + G - 1.
-  __device__ __forceinline__ void finish_wave(float* __restrict__ partial, size_t row0, int pidx,
-                                              int n_parts) {
+  // Sum the lane groups of the wavefront (every group scanned other rows).
+  __device__ __forceinline__ void reduce_slots() {
 #pragma unroll
     for (int off = LPT; off < kWave; off <<= 1) {
 #pragma unroll
@@ -170,6 +172,13 @@ struct CodedPV {
         }
       }
     }
+  }
+
+  // Partial state of this wavefront as partial `pidx` of `n_parts` for query
+  // heads row0 .. row0 + G - 1.
+  __device__ __forceinline__ void finish_wave(float* __restrict__ partial, size_t row0, int pidx,
+                                              int n_parts) {
+    reduce_slots();
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float l_w = wave_sum(l_lane[g]);
@@ -186,6 +195,60 @@ struct CodedPV {
       if (lane == 0) {
         part[0] = m_run[g];
         part[1] = l_w;
+      }
+    }
+  }
+
+  static constexpr int MERGE_FLOATS = WAVES * G * (2 * D + 2);
+
+  // The wavefronts of the workgroup merged through `scratch` (MERGE_FLOATS
+  // floats of LDS, free to reuse: the caller synchronizes before), written as
+  // partial `split` of `n_parts`.
+  __device__ __forceinline__ void finish(float* scratch, int tid, float* __restrict__ partial,
+                                         size_t row0, int split, int n_parts) {
+    reduce_slots();
+    float l_w[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) l_w[g] = wave_sum(l_lane[g]);
+    float* wm = scratch;                  // [WAVES][G]
+    float* wl = scratch + WAVES * G;      // [WAVES][G]
+    float* wo = scratch + 2 * WAVES * G;  // [WAVES][G][2D]: o, then a
+    if (lane < LPT) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          wo[(wave * G + g) * 2 * D + dblk * 8 + k] = o[g][k];
+          wo[(wave * G + g) * 2 * D + D + dblk * 8 + k] = QJLV ? 2.f * acc[g][k] - spn[g] : 0.f;
+        }
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        wm[wave * G + g] = m_run[g];
+        wl[wave * G + g] = l_w[g];
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < G * 2 * D; e += WAVES * kWave) {
+      const int g = e / (2 * D), dd = e % (2 * D);
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) Mx = fmaxf(Mx, wm[w * G + g]);
+      float num = 0.f, den = 0.f;
+      if (Mx != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+          const float f = exp2f(wm[w * G + g] - Mx);
+          num += f * wo[(w * G + g) * 2 * D + dd];
+          den += f * wl[w * G + g];
+        }
+      }
+      float* part = partial + ((row0 + g) * n_parts + split) * WIDTH;
+      part[4 + dd] = num;
+      if (dd == 0) {
+        part[0] = Mx;
+        part[1] = den;
       }
     }
   }

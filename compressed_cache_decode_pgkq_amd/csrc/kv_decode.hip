@@ -30,9 +30,11 @@ kv_merge_kernel(const float* __restrict__ partial, float* __restrict__ out, cons
   const int tid = threadIdx.x;
   __shared__ float s_a[128];
   float Mx = -INFINITY;
+#pragma unroll 8
   for (int p = 0; p < n_parts; ++p) Mx = fmaxf(Mx, part[size_t(p) * width]);
   float num = 0.f, an = 0.f, den = 0.f;
   if (tid < d && Mx != -INFINITY) {
+#pragma unroll 4
     for (int p = 0; p < n_parts; ++p) {
       const float* pp = part + size_t(p) * width;
       const float f = exp2f(pp[0] - Mx);
@@ -48,6 +50,7 @@ kv_merge_kernel(const float* __restrict__ partial, float* __restrict__ out, cons
     if (qjl) {
       // kappa S^T a: column tid of S_v[h], rows j < m = d
       const float* S = Sv + size_t(h) * d * d + tid;
+#pragma unroll 8
       for (int j = 0; j < d; ++j) corr = fmaf(S[size_t(j) * d], s_a[j], corr);
       corr *= 1.2533141373155003f / float(d);  // sqrt(pi/2) / m
     }

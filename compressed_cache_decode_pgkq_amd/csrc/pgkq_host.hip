@@ -538,7 +538,7 @@ static pgkq_status check_kv(const pgkq_params* pk, const pgkq_params* pv, Geomet
 static size_t kv_ws(const Geometry& gk, int64_t n_seq, int64_t n_q, const Splits& sp) {
   const pgkq::PrepLayout pl{gk.d, gk.n(), 1 << gk.ba, gk.m};
   return round_up(size_t(n_seq) * n_q * pl.stride() * sizeof(float), 256) +
-         round_up(size_t(n_seq) * n_q * 4 * sp.n * (2 * gk.d + 4) * sizeof(float), 256);
+         round_up(size_t(n_seq) * n_q * sp.partials() * (2 * gk.d + 4) * sizeof(float), 256);
 }
 
 size_t pgkq_kv_decode_workspace_bytes(const pgkq_params* pk, const pgkq_params* pv, int64_t n_seq,
@@ -627,7 +627,7 @@ pgkq_status pgkq_kv_decode_attn(const pgkq_params* pk, const pgkq_params* pv, co
     if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
       return PGKQ_ERR_HIP;
   }
-  return map_hip(pgkq::launch_kv_merge(a, g.d, 4 * sp.n, s));
+  return map_hip(pgkq::launch_kv_merge(a, g.d, sp.partials(), s));
 }
 
 pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,

@@ -73,7 +73,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   constexpr int NC = N * P / 32;
   constexpr int NW = NC + M / 32;
   constexpr int NQT = QJL ? (M / 4) * 16 * G : 1;
-  constexpr int MERGE_FLOATS = CODED_V ? 0 : SoftmaxPV<D, G, kScanWaves>::MERGE_FLOATS;
+  constexpr int MERGE_FLOATS = VP::MERGE_FLOATS;
   constexpr int MAIN_FLOATS = SS::TABLE_FLOATS > MERGE_FLOATS ? SS::TABLE_FLOATS : MERGE_FLOATS;
   (void)BA;
 
@@ -263,9 +263,14 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     }
   }
   if constexpr (CODED_V && !LOGITS) {
-    // every wavefront writes its own partial state (the merge applies S^T)
-    sm.finish_wave(a.partial, size_t(b) * a.n_q + size_t(h) * G, split * kScanWaves + wave,
-                   a.n_splits * kScanWaves);
+    // partial states only (the merge kernel applies S_v^T)
+    const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
+    if (a.wave_parts) {
+      sm.finish_wave(a.partial, row0, split * kScanWaves + wave, a.n_splits * kScanWaves);
+    } else {
+      __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
+      sm.finish(s_tab, tid, a.partial, row0, split, a.n_splits);
+    }
   } else if constexpr (!LOGITS) {
     const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
     if (a.wave_parts) {
