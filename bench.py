@@ -202,7 +202,7 @@ def main():
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; use --gpus 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; use --gpus 1"}))
         sys.exit(2)
 
     import torch
@@ -223,8 +223,8 @@ def main():
     import compressed_cache_decode_pgkq_amd as api
     from synth import CONFIGS
 
-    cfg = CONFIGS["c3"]           # decode workload
-    ecfg = CONFIGS["c4"]          # the same keys, encoded with the reorder step
+    cfg = CONFIGS["gqa_b16_t32k"]           # decode workload
+    ecfg = CONFIGS["gqa_b16_t32k_encode"]          # the same keys, encoded with the reorder step
     inp = generate(cfg)
     p = api.PgkqParams(cfg.head_dim, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
     n_seq, n_kv, T, d = inp["K"].shape

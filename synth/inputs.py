@@ -72,23 +72,23 @@ class WorkloadConfig:
 CONFIGS = {
     # NanoGPT-256 cache, one decode step: 6 layers x 4 heads flattened into 24
     # kv-heads (= query heads), head_dim 64, 128 cached tokens.
-    "c1": WorkloadConfig("c1", 1, 1, 24, 24, 128, 64, 3, 2, 64, "f32", "f32", 2, 8.0,
+    "nano_t128": WorkloadConfig("nano_t128", 1, 1, 24, 24, 128, 64, 3, 2, 64, "f32", "f32", 2, 8.0,
                          description="NanoGPT-256 cache, 6Lx4H, d64, T128, B1, b3/2, QJL m64"),
     # Full NanoGPT-256 context, batch 64.
-    "c2a": WorkloadConfig("c2a", 2, 64, 24, 24, 512, 64, 3, 2, 64, "f32", "f32", 2, 8.0,
+    "nano_b64_t512": WorkloadConfig("nano_b64_t512", 2, 64, 24, 24, 512, 64, 3, 2, 64, "f32", "f32", 2, 8.0,
                           description="NanoGPT-256 full context, B64, d64, T512, b3/2, QJL m64"),
-    "c2b": WorkloadConfig("c2b", 2, 64, 24, 24, 512, 64, 4, 3, 0, "f32", "f32", 2, 8.0,
+    "nano_b64_t512_b4": WorkloadConfig("nano_b64_t512_b4", 2, 64, 24, 24, 512, 64, 4, 3, 0, "f32", "f32", 2, 8.0,
                           description="NanoGPT-256 full context, B64, d64, T512, b4/3, no QJL"),
     # GQA decode at scale.
-    "c3": WorkloadConfig("c3", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,
+    "gqa_b16_t32k": WorkloadConfig("gqa_b16_t32k", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,
                          n_splits=8,
                          description="GQA 32q/8kv, d128, T32768, B16, b3/2, QJL m128, split-K"),
-    # Bulk encode: the 4 194 304 keys of the c3 cache, with the channel reorder step.
-    "c4": WorkloadConfig("c4", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,
+    # Bulk encode: the 4 194 304 keys of the 32k-token GQA cache, with the channel reorder step.
+    "gqa_b16_t32k_encode": WorkloadConfig("gqa_b16_t32k_encode", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,
                          reorder=True,
                          description="bulk encode of 4194304 fp16 keys, d128, reorder on, b3/2, QJL m128"),
     # Long context, one stream.
-    "c5": WorkloadConfig("c5", 5, 1, 32, 8, 131072, 128, 4, 3, 128, "f16", "bf16", 4, 10.0,
+    "gqa_b1_t131k": WorkloadConfig("gqa_b1_t131k", 5, 1, 32, 8, 131072, 128, 4, 3, 128, "f16", "bf16", 4, 10.0,
                          n_splits=256,
                          description="GQA 32q/8kv, d128, T131072, B1, b4/3, QJL m128, 256 splits"),
 }

@@ -84,14 +84,14 @@ def _run_full(cfg, samples, n_splits):
 
 
 def test_c3_full_size_sampled():
-    _run_full(CONFIGS["c3"], [(0, 0), (7, 3), (15, 7)], n_splits=CONFIGS["c3"].n_splits)
+    _run_full(CONFIGS["gqa_b16_t32k"], [(0, 0), (7, 3), (15, 7)], n_splits=CONFIGS["gqa_b16_t32k"].n_splits)
 
 
 def test_c5_full_size_sampled():
-    _run_full(CONFIGS["c5"], [(0, 0), (0, 5)], n_splits=CONFIGS["c5"].n_splits)
+    _run_full(CONFIGS["gqa_b1_t131k"], [(0, 0), (0, 5)], n_splits=CONFIGS["gqa_b1_t131k"].n_splits)
 
 
-@pytest.mark.parametrize("name", ["c2a", "c2b"])
+@pytest.mark.parametrize("name", ["nano_b64_t512", "nano_b64_t512_b4"])
 def test_c2_full_size_every_stream(name):
     cfg = CONFIGS[name]
     n_streams = [(b, h) for b in range(cfg.n_seq) for h in range(cfg.n_kv)]
@@ -100,7 +100,7 @@ def test_c2_full_size_every_stream(name):
 
 def test_c4_full_size_calibrate_and_encode_sampled():
     api = _api()
-    cfg = CONFIGS["c4"]
+    cfg = CONFIGS["gqa_b16_t32k_encode"]
     p = params_of(cfg)
     lp = lib_params(p)
     inp = make_inputs(cfg, with_values=False)
@@ -123,13 +123,13 @@ def test_c4_full_size_calibrate_and_encode_sampled():
         f = encode.encode_keys(K[b, h], signs[h], perms[h], tables[h][0], tables[h][1], S[h], p)
         got = layout.unpack_stream(codes[b, h].cpu().numpy(), p, cfg.n_tokens, cfg.n_tokens)
         merge_counts(counts, classify(f, got, tables[h][1], S[h], p))
-    print("c4 encode", counts)
+    print("bulk encode", counts)
     assert_code_parity(counts)
 
 
 def test_c2_fp16_comparator_full_size():
     api = _api()
-    cfg = CONFIGS["c2a"]
+    cfg = CONFIGS["nano_b64_t512"]
     inp = make_inputs(cfg)
     K16 = inp["K"].astype(np.float16)
     out = api.pgkq_fp16_decode_attn(q_tensor(inp["q"], cfg.q_dtype), to_dev(K16), to_dev(inp["V"]))
@@ -146,7 +146,7 @@ def test_c2_fp16_comparator_full_size():
 # ------------------------------------------------------------------ controls and the next rows at full size
 
 def _c3_inputs():
-    cfg = CONFIGS["c3"]
+    cfg = CONFIGS["gqa_b16_t32k"]
     return cfg, make_inputs(cfg)
 
 
@@ -192,7 +192,7 @@ def test_c3_fp16_comparator_full_size_sampled():
         ref, _ = attn.fp16_attention(q[b:b + 1, h * 4:h * 4 + 4], K16[b:b + 1, h:h + 1],
                                      V[b:b + 1, h:h + 1])
         worst = max(worst, float(np.abs(out[b, h * 4:h * 4 + 4] - ref[0]).max()))
-    print("fp16 c3 max-abs", worst)
+    print("fp16 32k-token cache max-abs", worst)
     assert worst <= OUT_TOL
 
 

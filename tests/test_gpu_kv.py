@@ -85,15 +85,15 @@ class KVCase:
 
 
 KV_CASES = {
-    "k3v3_d64_nanogpt": (CONFIGS["c1"], 3, {}),
-    "k3v3_d64_b2": (CONFIGS["c2a"].with_(n_seq=2), 3, {}),
-    "k3v3_d128_gqa": (CONFIGS["c3"].with_(n_seq=2, n_tokens=1000), 3, {}),
-    "k2v2_d128": (CONFIGS["c3"].with_(n_seq=1, n_tokens=700, b_main=2, b_angle=1), 2, {}),
-    "k4v4_d128_long": (CONFIGS["c5"].with_(n_tokens=3000), 4, {}),
-    "k3v2_d128": (CONFIGS["c3"].with_(n_seq=1, n_tokens=700), 2, {}),
-    "k4v2_d128": (CONFIGS["c5"].with_(n_tokens=900), 2, {}),
-    "k4v4_d64_noqjl": (CONFIGS["c2b"].with_(n_seq=2), 4, {}),
-    "k3v3_reorder": (CONFIGS["c4"].with_(n_seq=1, n_tokens=600), 3, {"reorder": True}),
+    "k3v3_d64_nanogpt": (CONFIGS["nano_t128"], 3, {}),
+    "k3v3_d64_b2": (CONFIGS["nano_b64_t512"].with_(n_seq=2), 3, {}),
+    "k3v3_d128_gqa": (CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=1000), 3, {}),
+    "k2v2_d128": (CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=700, b_main=2, b_angle=1), 2, {}),
+    "k4v4_d128_long": (CONFIGS["gqa_b1_t131k"].with_(n_tokens=3000), 4, {}),
+    "k3v2_d128": (CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=700), 2, {}),
+    "k4v2_d128": (CONFIGS["gqa_b1_t131k"].with_(n_tokens=900), 2, {}),
+    "k4v4_d64_noqjl": (CONFIGS["nano_b64_t512_b4"].with_(n_seq=2), 4, {}),
+    "k3v3_reorder": (CONFIGS["gqa_b16_t32k_encode"].with_(n_seq=1, n_tokens=600), 3, {"reorder": True}),
 }
 
 
@@ -138,7 +138,7 @@ def test_kv_value_encode_matches_oracle(name):
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_kv_group_sizes(group):
-    cfg = CONFIGS["c3"].with_(n_seq=1, n_kv=4, n_q=4 * group, n_tokens=500)
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_kv=4, n_q=4 * group, n_tokens=500)
     case = KVCase(cfg, 3)
     err = float(np.abs(case.gpu_decode(0) - case.oracle_out()).max())
     assert err <= OUT_TOL, err
@@ -146,7 +146,7 @@ def test_kv_group_sizes(group):
 
 @pytest.mark.parametrize("T", [1, 63, 65, 777])
 def test_kv_ragged_lengths(T):
-    case = KVCase(CONFIGS["c3"].with_(n_seq=1, n_tokens=1000), 3, n_tokens=T, capacity=1024)
+    case = KVCase(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=1000), 3, n_tokens=T, capacity=1024)
     want = case.oracle_out()
     for ns in (0, 3, 9):
         err = float(np.abs(case.gpu_decode(ns) - want).max())
@@ -156,7 +156,7 @@ def test_kv_ragged_lengths(T):
 def test_kv_garbage_beyond_the_cache_is_ignored():
     """Slots past n_tokens may hold any bits (a norm that reads as NaN or inf
     included): they carry no weight."""
-    case = KVCase(CONFIGS["c3"].with_(n_seq=1, n_tokens=1000), 3, n_tokens=700, capacity=1024)
+    case = KVCase(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=1000), 3, n_tokens=700, capacity=1024)
     cv = case.oracle_v_codes()
     rng = np.random.default_rng(0)
     k = case.k

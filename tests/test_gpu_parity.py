@@ -38,12 +38,12 @@ def _api():
 
 
 SMALL = {
-    "c1": (CONFIGS["c1"], {}),
-    "c2a": (CONFIGS["c2a"].with_(n_seq=3), {}),
-    "c2b": (CONFIGS["c2b"].with_(n_seq=3), {}),
-    "c3": (CONFIGS["c3"].with_(n_seq=2, n_tokens=1000), {}),
-    "c4": (CONFIGS["c4"].with_(n_seq=2, n_tokens=700), {"reorder": True}),
-    "c5": (CONFIGS["c5"].with_(n_tokens=3000), {}),
+    "nano_t128": (CONFIGS["nano_t128"], {}),
+    "nano_b64_t512": (CONFIGS["nano_b64_t512"].with_(n_seq=3), {}),
+    "nano_b64_t512_b4": (CONFIGS["nano_b64_t512_b4"].with_(n_seq=3), {}),
+    "gqa_b16_t32k": (CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=1000), {}),
+    "gqa_b16_t32k_encode": (CONFIGS["gqa_b16_t32k_encode"].with_(n_seq=2, n_tokens=700), {"reorder": True}),
+    "gqa_b1_t131k": (CONFIGS["gqa_b1_t131k"].with_(n_tokens=3000), {}),
 }
 
 
@@ -82,7 +82,7 @@ def test_encode_codes_match_oracle(name):
 
 
 def test_encode_without_hadamard():
-    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=500), hadamard=False)
+    case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=500), hadamard=False)
     counts = _code_counts(case, _gpu_encode(case))
     print(counts)
     assert_code_parity(counts)
@@ -90,7 +90,7 @@ def test_encode_without_hadamard():
 
 def test_encode_appends_at_token_offset():
     api = _api()
-    cfg = CONFIGS["c2a"].with_(n_seq=2, n_tokens=200)
+    cfg = CONFIGS["nano_b64_t512"].with_(n_seq=2, n_tokens=200)
     case = Case(cfg, capacity=256)
     dev = case.dev_inputs()
     p = lib_params(case.p)
@@ -105,7 +105,7 @@ def test_encode_appends_at_token_offset():
     assert np.array_equal(got, case.oracle_codes())
 
 
-@pytest.mark.parametrize("name", ["c1", "c2a", "c4"])
+@pytest.mark.parametrize("name", ["nano_t128", "nano_b64_t512", "gqa_b16_t32k_encode"])
 def test_calibrate_matches_oracle(name):
     api = _api()
     cfg, kw = SMALL[name]
@@ -167,20 +167,20 @@ def test_decode_matches_oracle_on_identical_codes(name, n_splits):
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_decode_group_sizes(group):
-    cfg = CONFIGS["c3"].with_(n_seq=2, n_kv=2, n_q=2 * group, n_tokens=600)
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_kv=2, n_q=2 * group, n_tokens=600)
     _check_decode(Case(cfg), n_splits=0)
 
 
 @pytest.mark.parametrize("qd", ["f32", "f16", "bf16"])
 def test_decode_query_dtypes(qd):
-    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=400))
+    case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=400))
     q = case.q.astype(np.float16).astype(np.float32) if qd == "f16" else case.q
     _check_decode(case, q_override=q, q_dtype=qd)
 
 
 @pytest.mark.parametrize("T", [1, 2, 63, 65, 257, 1000])
 def test_decode_ragged_lengths(T):
-    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=1000), n_tokens=T, capacity=1024)
+    case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=1000), n_tokens=T, capacity=1024)
     _check_decode(case, n_splits=0)
     _check_decode(case, n_splits=3)
     _check_decode(case, n_splits=9)
@@ -188,7 +188,7 @@ def test_decode_ragged_lengths(T):
 
 def test_decode_empty_cache_gives_zeros():
     api = _api()
-    case = Case(CONFIGS["c1"], n_tokens=0, capacity=128)
+    case = Case(CONFIGS["nano_t128"], n_tokens=0, capacity=128)
     dev = case.dev_inputs()
     out = torch.full((1, 24, 64), 7.0, device="cuda:0")
     api.pgkq_decode_attn(lib_params(case.p), q_tensor(case.q, "f32"),
@@ -203,7 +203,7 @@ def test_decode_empty_cache_gives_zeros():
 def test_ablation_grid_hadamard_by_qjl(hadamard, qjl):
     """The 2x2 of the ablation paragraph (Hadamard on/off x QJL on/off, b_main = 3):
     every cell encodes bit-exactly and decodes within the bars."""
-    cfg = CONFIGS["c2a"].with_(n_seq=2, qjl_m=64 if qjl else 0)
+    cfg = CONFIGS["nano_b64_t512"].with_(n_seq=2, qjl_m=64 if qjl else 0)
     case = Case(cfg, hadamard=hadamard)
     counts = _code_counts(case, _gpu_encode(case))
     print(hadamard, qjl, counts)
@@ -212,14 +212,14 @@ def test_ablation_grid_hadamard_by_qjl(hadamard, qjl):
 
 
 def test_decode_without_hadamard():
-    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=500), hadamard=False)
+    case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=500), hadamard=False)
     _check_decode(case)
 
 
 def test_end_to_end_calibrate_encode_decode():
     """GPU calibrate -> encode -> decode against oracle calibrate -> encode -> decode."""
     api = _api()
-    cfg = CONFIGS["c4"].with_(n_seq=2, n_tokens=900)
+    cfg = CONFIGS["gqa_b16_t32k_encode"].with_(n_seq=2, n_tokens=900)
     case = Case(cfg, reorder=True)
     p = lib_params(case.p)
     Kt = k_tensor(case.K)
@@ -259,7 +259,7 @@ def _fp16_check(cfg, n_splits=0, T=None, cap=None):
 
 
 @pytest.mark.parametrize("n_splits", [0, 1, 5, 40])
-@pytest.mark.parametrize("name", ["c2a", "c3"])
+@pytest.mark.parametrize("name", ["nano_b64_t512", "gqa_b16_t32k"])
 def test_fp16_comparator_matches_oracle(name, n_splits):
     cfg, _ = SMALL[name]
     _fp16_check(cfg, n_splits)
@@ -268,7 +268,7 @@ def test_fp16_comparator_matches_oracle(name, n_splits):
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 @pytest.mark.parametrize("d", [64, 128])
 def test_fp16_comparator_group_sizes(d, group):
-    base = CONFIGS["c2a"] if d == 64 else CONFIGS["c3"]
+    base = CONFIGS["nano_b64_t512"] if d == 64 else CONFIGS["gqa_b16_t32k"]
     cfg = base.with_(n_seq=1, n_kv=4, n_q=4 * group, n_tokens=700)
     _fp16_check(cfg, 0)
     _fp16_check(cfg, 6)
@@ -276,13 +276,13 @@ def test_fp16_comparator_group_sizes(d, group):
 
 @pytest.mark.parametrize("T", [1, 63, 65, 777])
 def test_fp16_comparator_ragged(T):
-    cfg = CONFIGS["c3"].with_(n_seq=1, n_tokens=1000)
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=1000)
     for ns in (0, 3, 9):
         _fp16_check(cfg, ns, T=T, cap=1024)
 
 
 def test_fp16_comparator_long_stream_wave_partitions():
-    _fp16_check(CONFIGS["c5"].with_(n_tokens=6000), 0)
+    _fp16_check(CONFIGS["gqa_b1_t131k"].with_(n_tokens=6000), 0)
 
 
 # ------------------------------------------------------------------ negative controls
@@ -307,7 +307,7 @@ def _decode_err(case, codes_np, tables=None, signs=None):
 
 @pytest.mark.parametrize("mutation", ["radius_code", "sign_words", "rht_signs", "codebook"])
 def test_negative_controls_break_parity(mutation):
-    case = Case(CONFIGS["c3"].with_(n_seq=1, n_tokens=256))
+    case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=256))
     good = case.oracle_codes()
     assert _decode_err(case, good) <= OUT_TOL
     bad = good.copy()

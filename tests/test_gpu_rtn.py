@@ -47,8 +47,8 @@ def _inputs(name, **over):
 
 
 SMALL = {
-    "d64_f32": ("c2a", dict(n_seq=2)),
-    "d128_f16": ("c3", dict(n_seq=2, n_tokens=1000)),
+    "d64_f32": ("nano_b64_t512", dict(n_seq=2)),
+    "d128_f16": ("gqa_b16_t32k", dict(n_seq=2, n_tokens=1000)),
 }
 
 
@@ -102,7 +102,7 @@ def test_rtn_encode_degenerate_keys(bits):
 
 
 def test_rtn_encode_appends_at_token_offset():
-    cfg, inp = _inputs("c2a", n_seq=2)
+    cfg, inp = _inputs("nano_b64_t512", n_seq=2)
     K = inp["K"]
     T = K.shape[2]
     cap = T + 16
@@ -154,7 +154,7 @@ def _logit_bound(q, codes, scale, zp):
 @pytest.mark.parametrize("bits", [3, 4])
 def test_rtn_logits_within_fp32_bound(bits):
     api = _api()
-    cfg, inp = _inputs("c3", n_seq=2, n_tokens=1000)
+    cfg, inp = _inputs("gqa_b16_t32k", n_seq=2, n_tokens=1000)
     K = inp["K"].astype(np.float64)
     q = inp["q"]
     n_seq, n_kv, T, d = K.shape
@@ -176,13 +176,13 @@ def test_rtn_logits_within_fp32_bound(bits):
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_rtn_group_sizes(group):
-    cfg, inp = _inputs("c3", n_seq=1, n_tokens=600, n_q=8 * group)
+    cfg, inp = _inputs("gqa_b16_t32k", n_seq=1, n_tokens=600, n_q=8 * group)
     _check_decode(inp["K"], inp["V"], inp["q"], cfg.q_dtype, 4)
 
 
 @pytest.mark.parametrize("T", [1, 63, 65, 777])
 def test_rtn_ragged_lengths(T):
-    cfg, inp = _inputs("c3", n_seq=1, n_tokens=1000)
+    cfg, inp = _inputs("gqa_b16_t32k", n_seq=1, n_tokens=1000)
     for ns in (0, 3, 9):
         _check_decode(inp["K"], inp["V"], inp["q"], cfg.q_dtype, 3, ns, T=T, cap=1024)
 
@@ -190,7 +190,7 @@ def test_rtn_ragged_lengths(T):
 def test_rtn_long_stream_wave_partitions():
     """One sequence, few streams: the automatic split runs one partition per
     wavefront (the long-context launch shape)."""
-    cfg, inp = _inputs("c5", n_tokens=6000)
+    cfg, inp = _inputs("gqa_b1_t131k", n_tokens=6000)
     _check_decode(inp["K"], inp["V"], inp["q"], cfg.q_dtype, 4, 0)
     _check_decode(inp["K"], inp["V"], inp["q"], cfg.q_dtype, 4, 48)
 
@@ -211,7 +211,7 @@ def test_rtn_negative_controls_break_parity(mutation):
     """A planted mistake in the oracle's records (CPU side) must fail the logit
     bar: the comparison can tell."""
     api = _api()
-    cfg, inp = _inputs("c2a", n_seq=1)
+    cfg, inp = _inputs("nano_b64_t512", n_seq=1)
     K = inp["K"][:, :2].astype(np.float64)
     q = inp["q"][:, :2]
     n_seq, n_kv, T, d = K.shape
@@ -240,7 +240,7 @@ def test_rtn_negative_controls_break_parity(mutation):
 def test_rtn_end_to_end_encode_then_decode():
     """GPU encode, then GPU decode of those records, against the oracle."""
     api = _api()
-    cfg, inp = _inputs("c3", n_seq=2, n_tokens=1000)
+    cfg, inp = _inputs("gqa_b16_t32k", n_seq=2, n_tokens=1000)
     K, V, q = inp["K"], inp["V"], inp["q"]
     recs = _gpu_records(K, 3, K.shape[2])
     out = api.pgkq_rtn_decode_attn(q_tensor(q, cfg.q_dtype), recs, to_dev(V), 3)

@@ -65,12 +65,12 @@ def _counts(case, got, t):
 
 
 STEP_CASES = {
-    "d64_qjl_f32": (CONFIGS["c2a"].with_(n_seq=2, n_tokens=300), {}),
-    "d64_noqjl": (CONFIGS["c2b"].with_(n_seq=2, n_tokens=300), {}),
-    "d128_qjl_f16": (CONFIGS["c3"].with_(n_seq=2, n_tokens=700), {}),
-    "d128_reorder": (CONFIGS["c4"].with_(n_seq=1, n_tokens=500), {"reorder": True}),
-    "d128_b4": (CONFIGS["c5"].with_(n_tokens=900), {}),
-    "no_hadamard": (CONFIGS["c3"].with_(n_seq=1, n_tokens=400), {"hadamard": False}),
+    "d64_qjl_f32": (CONFIGS["nano_b64_t512"].with_(n_seq=2, n_tokens=300), {}),
+    "d64_noqjl": (CONFIGS["nano_b64_t512_b4"].with_(n_seq=2, n_tokens=300), {}),
+    "d128_qjl_f16": (CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=700), {}),
+    "d128_reorder": (CONFIGS["gqa_b16_t32k_encode"].with_(n_seq=1, n_tokens=500), {"reorder": True}),
+    "d128_b4": (CONFIGS["gqa_b1_t131k"].with_(n_tokens=900), {}),
+    "no_hadamard": (CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=400), {"hadamard": False}),
 }
 
 
@@ -108,7 +108,7 @@ def test_decode_step_loop_matches_oracle_every_step():
     """Six consecutive steps on one cache: after each, the output equals the
     oracle's decode over the cache grown so far (auto and fixed splits)."""
     api = _api()
-    cfg = CONFIGS["c3"].with_(n_seq=1, n_tokens=506)
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=506)
     case = Case(cfg, capacity=512)
     dev = case.dev_inputs()
     p = lib_params(case.p)
@@ -136,7 +136,7 @@ def test_decode_step_equals_encode_then_decode_when_codes_agree():
     """Where the appended record equals the bulk encoder's, the step's output is
     the output of pgkq_encode + pgkq_decode_attn on the same cache, bit for bit."""
     api = _api()
-    cfg = CONFIGS["c3"].with_(n_seq=2, n_tokens=333)
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=333)
     case = Case(cfg, capacity=336)
     dev = case.dev_inputs()
     p = lib_params(case.p)
