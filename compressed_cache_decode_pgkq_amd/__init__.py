@@ -22,6 +22,7 @@ from .api import (  # noqa: F401
     pgkq_kv_decode_attn,
     pgkq_kv_decode_workspace_bytes,
     pgkq_lloyd_max_beta,
+    pgkq_lloyd_max_empirical,
     pgkq_record_bytes,
     pgkq_rtn_decode_attn,
     pgkq_rtn_decode_workspace_bytes,

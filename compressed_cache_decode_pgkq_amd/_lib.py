@@ -59,6 +59,9 @@ SIGNATURES = {
     "pgkq_codes_bytes": (_sz, [_P, _i64, _i64]),
     "pgkq_lloyd_max_beta": (ctypes.c_int, [_i32, _i32, ctypes.POINTER(ctypes.c_double),
                                            ctypes.POINTER(ctypes.c_double)]),
+    "pgkq_lloyd_max_empirical": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), _i64, _i32,
+                                                ctypes.POINTER(ctypes.c_double),
+                                                ctypes.POINTER(ctypes.c_double)]),
     "pgkq_calibrate_workspace_bytes": (_sz, [_P, _i64, _i64, _i64]),
     "pgkq_calibrate": (ctypes.c_int, [_P, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),

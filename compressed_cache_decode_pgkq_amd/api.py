@@ -90,6 +90,18 @@ def pgkq_lloyd_max_beta(head_dim: int, b_main: int):
     return np.array(lv[:], dtype=np.float64), np.array(th[: n - 1], dtype=np.float64)
 
 
+def pgkq_lloyd_max_empirical(samples, b_main: int):
+    """Lloyd-Max table refit on a host sample of rho values -> (levels, thresholds)."""
+    x = np.ascontiguousarray(np.asarray(samples, dtype=np.float64).ravel())
+    n = 1 << b_main
+    lv = (ctypes.c_double * n)()
+    th = (ctypes.c_double * max(n - 1, 1))()
+    L.check(L.lib().pgkq_lloyd_max_empirical(
+        x.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), x.size, b_main, lv, th),
+        "pgkq_lloyd_max_empirical")
+    return np.array(lv[:], dtype=np.float64), np.array(th[: n - 1], dtype=np.float64)
+
+
 def pgkq_calibrate(params: PgkqParams, K: torch.Tensor, reorder: bool = False, stream=None):
     """K [n_seq, n_kv, n_tokens, d] -> (sumsq [n_kv, d] f64, perm [n_kv, d] i16 bits of u16,
     codebook [n_kv, 2L] f32)."""

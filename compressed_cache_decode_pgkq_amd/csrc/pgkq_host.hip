@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -233,6 +234,52 @@ pgkq_status lloyd_max(int head_dim, int b_main, double* levels, double* threshol
   return PGKQ_OK;
 }
 
+// Lloyd-Max on an empirical sample (the PGKQ-KV' refit).  The sample is
+// sorted once; a cell is then a contiguous run of it: with thresholds t_j, the
+// samples coded j (#{t : t < x} = j) are those with t_{j-1} < x <= t_j, whose
+// end index is the upper bound of t_j.  Cell sums are compensated (Neumaier),
+// so a level is its cell's mean to a few ulps whatever the cell size.
+double cell_mean(const double* x, int64_t lo, int64_t hi) {
+  double s = 0.0, comp = 0.0;
+  for (int64_t i = lo; i < hi; ++i) {
+    const double t = s + x[i];
+    comp += std::fabs(s) >= std::fabs(x[i]) ? (s - t) + x[i] : (x[i] - t) + s;
+    s = t;
+  }
+  return (s + comp) / double(hi - lo);
+}
+
+pgkq_status lloyd_max_samples(const double* samples, int64_t n, int b_main, double* levels,
+                              double* thresholds) {
+  const int L = 1 << b_main;
+  std::vector<double> x(samples, samples + n);
+  std::sort(x.begin(), x.end());
+  std::vector<double> c(L), t(L - 1);
+  std::vector<int64_t> end(L), prev_end(L, -1);
+  for (int j = 0; j < L; ++j) c[j] = x[static_cast<int64_t>((j + 0.5) * double(n) / L)];
+  bool done = false;
+  for (int it = 0; it < 100000 && !done; ++it) {
+    for (int j = 0; j + 1 < L; ++j) t[j] = 0.5 * (c[j] + c[j + 1]);
+    for (int j = 0; j + 1 < L; ++j)
+      end[j] = std::upper_bound(x.begin(), x.end(), t[j]) - x.begin();
+    end[L - 1] = n;
+    if (end == prev_end) {
+      done = true;
+      break;
+    }
+    int64_t lo = 0;
+    for (int j = 0; j < L; ++j) {
+      if (end[j] > lo) c[j] = cell_mean(x.data(), lo, end[j]);
+      lo = std::max(lo, end[j]);
+    }
+    prev_end = end;
+  }
+  if (!done) return PGKQ_ERR_UNSUPPORTED;
+  for (int j = 0; j < L; ++j) levels[j] = c[j];
+  for (int j = 0; j + 1 < L; ++j) thresholds[j] = 0.5 * (c[j] + c[j + 1]);
+  return PGKQ_OK;
+}
+
 struct TableCache {
   std::mutex mu;
   bool have[2][5] = {};
@@ -292,6 +339,21 @@ pgkq_status pgkq_lloyd_max_beta(int32_t head_dim, int32_t b_main, double* levels
   if (b_main < 1 || b_main > 8) return PGKQ_ERR_UNSUPPORTED;
   try {
     return lloyd_max(head_dim, b_main, levels_host, thresholds_host);
+  } catch (...) {
+    return PGKQ_ERR_HIP;
+  }
+}
+
+pgkq_status pgkq_lloyd_max_empirical(const double* samples_host, int64_t n_samples,
+                                     int32_t b_main, double* levels_host,
+                                     double* thresholds_host) {
+  if (!samples_host || !levels_host || !thresholds_host) return PGKQ_ERR_NULL;
+  if (b_main < 1 || b_main > 8) return PGKQ_ERR_UNSUPPORTED;
+  if (n_samples < (int64_t(1) << b_main)) return PGKQ_ERR_SHAPE;
+  for (int64_t i = 0; i < n_samples; ++i)
+    if (!std::isfinite(samples_host[i])) return PGKQ_ERR_UNSUPPORTED;
+  try {
+    return lloyd_max_samples(samples_host, n_samples, b_main, levels_host, thresholds_host);
   } catch (...) {
     return PGKQ_ERR_HIP;
   }

@@ -110,6 +110,27 @@ size_t pgkq_codes_bytes(const pgkq_params* p, int64_t n_streams, int64_t capacit
 pgkq_status pgkq_lloyd_max_beta(int32_t head_dim, int32_t b_main, double* levels_host,
                                 double* thresholds_host);
 
+/* Host routine.  Lloyd-Max quantizer refit on a sample of rho values (the
+ * empirical-refit variant PGKQ-KV' of the PGKQ-KV paragraphs: the codebook
+ * fitted to a short activation capture instead of the Beta prior).  The sample
+ * is rho = r sqrt(d/2) / s_h for the pairs of captured rows (r the pair radius,
+ * s_h the head's radius scale), so the result is scaled into a codebook by
+ * s_h / sqrt(d/2) exactly like the Beta table.
+ *   samples_host [n_samples] float64, HOST memory, finite, not modified;
+ *                n_samples >= 2^b_main (else PGKQ_ERR_SHAPE)
+ *   levels_host  out [2^b_main] float64, ascending
+ *   thresholds_host out [2^b_main - 1] float64, midpoints of adjacent levels
+ * Start: the sorted sample at index floor((j + 1/2) n / 2^b_main).  Step:
+ * thresholds at midpoints, every sample in the cell #{t_j < rho} (the encoder's
+ * decision rule), each non-empty cell's level set to the cell's mean (an empty
+ * cell keeps its level).  Stops at the fixed point where no sample changes
+ * cell; PGKQ_ERR_UNSUPPORTED if none is reached in 100000 steps, if b_main is
+ * outside 1..8 or a sample is not finite.  Deterministic; allocates host memory
+ * for a sorted copy of the sample. */
+pgkq_status pgkq_lloyd_max_empirical(const double* samples_host, int64_t n_samples,
+                                     int32_t b_main, double* levels_host,
+                                     double* thresholds_host);
+
 /* Bytes of workspace pgkq_calibrate needs. */
 size_t pgkq_calibrate_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_kv,
                                       int64_t n_tokens);

@@ -112,6 +112,47 @@ def lloyd_max_beta(head_dim: int, b_main: int, tol: float = 1e-13, max_iter: int
     return c, t
 
 
+def lloyd_max_empirical(samples, b_main: int, max_iter: int = 100000, history: bool = False):
+    """Lloyd-Max quantizer fitted to samples of rho (the empirical refit of the
+    PGKQ-KV paragraphs, PGKQ-KV': the same two conditions as for the prior,
+    with the sample distribution in place of the Beta density).
+
+    Start: the sample quantiles at (j + 1/2) / L (sorted sample at index
+    floor((j + 1/2) N / L)).  Step: thresholds at the midpoints of adjacent
+    levels; a sample goes to the cell #{j : t_j < rho} (the decision rule of
+    the encoder); each level becomes the mean of its cell (an empty cell keeps
+    its level).  Stops when no sample changes cell, i.e. at a fixed point
+    where every level is exactly its cell's mean.  Returns (levels, thresholds)
+    float64; with ``history`` also the mean squared error after every step.
+    """
+    x = np.sort(np.asarray(samples, dtype=np.float64).ravel())
+    N = x.size
+    L = 1 << b_main
+    if N < L or L < 2:
+        raise ValueError("need at least 2^b_main samples and b_main >= 1")
+    c = x[((np.arange(L) + 0.5) * N / L).astype(np.int64)].copy()
+    cells = None
+    hist = []
+    for _ in range(max_iter):
+        t = 0.5 * (c[:-1] + c[1:])
+        new_cells = np.sum(t[None, :] < x[:, None], axis=1)
+        if cells is not None and np.array_equal(new_cells, cells):
+            break
+        cells = new_cells
+        for j in range(L):
+            members = x[cells == j]
+            if members.size:
+                c[j] = members.mean()
+        if history:
+            hist.append(float(np.mean((x - c[cells]) ** 2)))
+    else:  # pragma: no cover - the assignment sequence is finite
+        raise RuntimeError("empirical Lloyd-Max did not converge")
+    t = 0.5 * (c[:-1] + c[1:])
+    if history:
+        return c, t, hist
+    return c, t
+
+
 def scaled_table(levels, thresholds, head_scale: float, head_dim: int):
     """Per-head table in radius units, rounded to fp32: (levels32, thresholds32).
 

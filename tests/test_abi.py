@@ -80,6 +80,44 @@ def test_host_lloyd_max_rejects():
     assert lib.pgkq_lloyd_max_beta(64, 0, lv, th) == L.PGKQ_ERR_UNSUPPORTED
 
 
+def _refit_samples(kind):
+    rng = np.random.default_rng(5)
+    if kind == "halfnormal":
+        return np.abs(rng.standard_normal(20000)) * 1.7
+    if kind == "prior":
+        return codebook.rho_quantile(rng.random(30000), 64)
+    if kind == "ties":   # heavy duplicates, some cells may empty
+        return rng.integers(0, 12, size=3000).astype(np.float64) * 0.25
+    return rng.standard_normal(16) + 3.0   # exactly 2^b samples at b = 4
+
+
+@pytest.mark.parametrize("kind,b", [("halfnormal", 2), ("halfnormal", 3), ("prior", 4),
+                                    ("ties", 3), ("minimal", 4)])
+def test_host_empirical_lloyd_max_matches_oracle(kind, b):
+    x = _refit_samples(kind)
+    lv, th = api.pgkq_lloyd_max_empirical(x, b)
+    c, t = codebook.lloyd_max_empirical(x, b)
+    np.testing.assert_allclose(lv, c, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(th, t, rtol=1e-12, atol=1e-14)
+
+
+def test_host_empirical_lloyd_max_rejects():
+    lv = (ctypes.c_double * 16)()
+    th = (ctypes.c_double * 16)()
+    lib = L.lib()
+    x = np.abs(np.random.default_rng(0).standard_normal(64))
+    xp = x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    assert lib.pgkq_lloyd_max_empirical(None, 64, 3, lv, th) == L.PGKQ_ERR_NULL
+    assert lib.pgkq_lloyd_max_empirical(xp, 64, 3, None, th) == L.PGKQ_ERR_NULL
+    assert lib.pgkq_lloyd_max_empirical(xp, 7, 3, lv, th) == L.PGKQ_ERR_SHAPE
+    assert lib.pgkq_lloyd_max_empirical(xp, 64, 0, lv, th) == L.PGKQ_ERR_UNSUPPORTED
+    assert lib.pgkq_lloyd_max_empirical(xp, 64, 9, lv, th) == L.PGKQ_ERR_UNSUPPORTED
+    y = x.copy()
+    y[5] = np.nan
+    assert lib.pgkq_lloyd_max_empirical(y.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), 64, 3,
+                                        lv, th) == L.PGKQ_ERR_UNSUPPORTED
+
+
 def _params(*prm):
     return ctypes.byref(L.PgkqParams(*prm))
 

@@ -704,3 +704,41 @@ def test_kv_decode_error_shrinks_with_bits():
         out, _ = kv.decode_kv(q, kf, vf, kt, vt, Sk, Sv, signs, None, pk, pv)
         errs.append(np.abs(out[0, 0] - exact).max())
     assert errs[0] > errs[1] > errs[2]
+
+
+# ------------------------------------------------------------------ empirical refit (PGKQ-KV')
+
+def test_empirical_lloyd_max_recovers_a_discrete_distribution():
+    """Samples on exactly L distinct values, equally often: the fixed point puts
+    one level on each value (each cell holds one value; zero error)."""
+    vals = np.array([0.3, 0.7, 1.1, 1.2, 2.0, 2.05, 3.5, 4.0])
+    x = np.repeat(vals, 50)
+    c, t, hist = codebook.lloyd_max_empirical(np.random.default_rng(1).permutation(x), 3,
+                                              history=True)
+    np.testing.assert_allclose(c, vals, rtol=0, atol=1e-15)
+    assert hist[-1] < 1e-28
+
+
+def test_empirical_lloyd_max_fixed_point_and_monotone_error():
+    rng = np.random.default_rng(7)
+    x = np.abs(rng.standard_normal(5000)) * 1.3
+    c, t, hist = codebook.lloyd_max_empirical(x, 3, history=True)
+    cells = np.sum(t[None, :] < x[:, None], axis=1)
+    for j in range(8):  # every level is its cell's mean, thresholds are midpoints
+        np.testing.assert_allclose(c[j], x[cells == j].mean(), rtol=1e-14)
+    np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=0)
+    assert all(b <= a + 1e-15 for a, b in zip(hist, hist[1:]))
+
+
+def test_empirical_lloyd_max_on_prior_samples_approaches_the_beta_table():
+    """Fitted to the prior's own quantiles at (i + 1/2)/N (a stratified sample of
+    the Beta radius law), the empirical table tends to the analytic one as N
+    grows."""
+    d, b = 64, 3
+    c_ref, _ = codebook.lloyd_max_beta(d, b)
+    errs = []
+    for N in (20000, 100000):
+        x = codebook.rho_quantile((np.arange(N) + 0.5) / N, d // 2)
+        c_emp, _ = codebook.lloyd_max_empirical(x, b)
+        errs.append(float(np.max(np.abs(c_emp - c_ref))))
+    assert errs[1] < 1e-3 and errs[1] < 0.5 * errs[0], errs
