@@ -38,7 +38,7 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_scan_gqa32k_b16_traffic
 SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/scan.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/pgkq_internal.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/coded_pv.hpp",
-                "compressed_cache_decode_pgkq_amd/csrc/softmax_pv.hpp",
+                "compressed_cache_decode_pgkq_amd/csrc/mfma_pv.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
 
 
@@ -123,7 +123,7 @@ def measure_copy(torch, dev, reps: int = 10) -> float:
     return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
-def run_controls(api, torch, dev, cfg, K, V, q, signs, S, flush, E, reps: int = 20):
+def run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E, reps: int = 20):
     """The same decode workload on the RTN INT4 / INT3 key caches, with PGKQ-coded
     values as well (PGKQ-KV k3v3), and on the uncompressed fp16 cache (same
     keys, values, queries and split count): scan kernel time and its share of
@@ -150,7 +150,7 @@ def run_controls(api, torch, dev, cfg, K, V, q, signs, S, flush, E, reps: int = 
         codes = api.pgkq_rtn_encode(K, bits)
         ws = torch.empty(api.pgkq_rtn_decode_workspace_bytes(d, n_seq, cfg.n_q, n_kv, T, cfg.n_splits),
                          dtype=torch.uint8, device=dev)
-        ms = timed(lambda: api.pgkq_rtn_decode_attn(q, codes, V, bits, n_splits=cfg.n_splits, out=out,
+        ms = timed(lambda: api.pgkq_rtn_decode_attn(q, codes, Vt, bits, n_splits=cfg.n_splits, out=out,
                                                     workspace=ws, events=(e0, e1)))
         alg = n_seq * n_kv * T * (rb + 2 * d)
         res[f"rtn_int{bits}"] = {"record_bytes": rb, "scan_ms": ms,
@@ -182,7 +182,7 @@ def run_controls(api, torch, dev, cfg, K, V, q, signs, S, flush, E, reps: int = 
     del ck, cv, ws
     ws = torch.empty(max(api.pgkq_fp16_decode_workspace_bytes(d, n_seq, cfg.n_q, n_kv, T, cfg.n_splits), 256),
                      dtype=torch.uint8, device=dev)
-    ms = timed(lambda: api.pgkq_fp16_decode_attn(q, K, V, n_splits=cfg.n_splits, out=out, workspace=ws,
+    ms = timed(lambda: api.pgkq_fp16_decode_attn(q, K, Vt, n_splits=cfg.n_splits, out=out, workspace=ws,
                                                  events=(e0, e1)))
     alg = n_seq * n_kv * T * 4 * d
     res["fp16_cache"] = {"record_bytes": 2 * d, "scan_ms": ms,
@@ -229,7 +229,8 @@ def main():
     p = api.PgkqParams(cfg.head_dim, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
     n_seq, n_kv, T, d = inp["K"].shape
     K = torch.from_numpy(inp["K"]).to(dev)
-    V = torch.from_numpy(inp["V"]).to(dev)
+    V = torch.from_numpy(inp["V"]).to(dev)      # value rows (encoded as keys by the PGKQ-KV control)
+    Vt = api.pgkq_pack_values(V)                  # the fp16 value cache, 32-token tiles
     q = torch.from_numpy(inp["q"]).to(torch.bfloat16).to(dev)
     signs = torch.from_numpy(inp["signs"]).to(dev)
     S = torch.from_numpy(inp["S"]).to(dev)
@@ -257,7 +258,7 @@ def main():
         flush.fill_(1)
         if ev:
             ev[3].record()
-        api.pgkq_decode_attn(p, q, codes, V, signs, perm, cb, S, n_splits=cfg.n_splits, out=out,
+        api.pgkq_decode_attn(p, q, codes, Vt, signs, perm, cb, S, n_splits=cfg.n_splits, out=out,
                              workspace=ws, events=(ev[5], ev[6]) if ev else None)
         if ev:
             ev[4].record()
@@ -282,7 +283,7 @@ def main():
     pct = lambda k: {"p10": float(np.percentile(ph[:, k], 10)), "p50": float(np.median(ph[:, k])),  # noqa: E731
                      "p90": float(np.percentile(ph[:, k], 90))}
     copy_gbs = measure_copy(torch, dev)
-    controls = run_controls(api, torch, dev, cfg, K, V, q, signs, S, flush, E)
+    controls = run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E)
 
     token_heads = n_seq * n_kv * T
     alg_bytes = token_heads * (rb + 2 * d)

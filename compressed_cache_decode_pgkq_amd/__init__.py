@@ -23,6 +23,7 @@ from .api import (  # noqa: F401
     pgkq_kv_decode_workspace_bytes,
     pgkq_lloyd_max_beta,
     pgkq_lloyd_max_empirical,
+    pgkq_pack_values,
     pgkq_record_bytes,
     pgkq_rtn_decode_attn,
     pgkq_rtn_decode_workspace_bytes,
@@ -30,6 +31,7 @@ from .api import (  # noqa: F401
     pgkq_rtn_logits,
     pgkq_rtn_record_bytes,
     pgkq_status_string,
+    pgkq_unpack_values,
     pgkq_version,
 )
 from ._lib import PgkqError  # noqa: F401

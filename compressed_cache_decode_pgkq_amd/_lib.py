@@ -62,6 +62,8 @@ SIGNATURES = {
     "pgkq_lloyd_max_empirical": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), _i64, _i32,
                                                 ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_double)]),
+    "pgkq_pack_values": (ctypes.c_int, [_vp, _i64, _i64, _i32, _vp, _i64, _i64, _vp]),
+    "pgkq_unpack_values": (ctypes.c_int, [_vp, _i64, _i64, _i32, _i64, _i64, _vp, _vp]),
     "pgkq_calibrate_workspace_bytes": (_sz, [_P, _i64, _i64, _i64]),
     "pgkq_calibrate": (ctypes.c_int, [_P, _vp, ctypes.c_int, _i64, _i64, _i64, _i32, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),

@@ -145,7 +145,8 @@ def pgkq_decode_workspace_bytes(params: PgkqParams, n_seq, n_q, n_kv, n_tokens, 
 def pgkq_decode_attn(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, V: torch.Tensor,
                      signs, perm, codebook, S, n_tokens=None, softmax_scale: float = 0.0,
                      n_splits: int = 0, out=None, workspace=None, events=None, stream=None):
-    """q [n_seq, n_q, d]; codes [n_seq, n_kv, cap * record]; V [n_seq, n_kv, cap, d] fp16."""
+    """q [n_seq, n_q, d]; codes [n_seq, n_kv, cap * record]; V the fp16 value cache
+    [n_seq, n_kv, cap, d] in 32-token tiles (pgkq_pack_values)."""
     n_seq, n_q, d = q.shape
     n_kv, cap = V.shape[1], V.shape[2]
     n_tok = cap if n_tokens is None else int(n_tokens)
@@ -221,9 +222,39 @@ def pgkq_status_string(status: int) -> str:
     return L.status_string(status)
 
 
+def pgkq_pack_values(rows: torch.Tensor, capacity=None, cache=None, slot_offset: int = 0,
+                     stream=None):
+    """fp16 value rows [n_seq, n_kv, T, d] -> the value cache [n_seq, n_kv, capacity, d] in
+    32-token tiles (slots [slot_offset, slot_offset + T) written; capacity defaults to T
+    rounded up to 32)."""
+    n_seq, n_kv, T, d = rows.shape
+    if cache is None:
+        cap = int(capacity) if capacity is not None else max(32, (T + 31) // 32 * 32)
+        cache = torch.zeros((n_seq, n_kv, cap, d), dtype=torch.float16, device=rows.device)
+    cap = cache.shape[2]
+    rows = rows.contiguous()
+    st = L.lib().pgkq_pack_values(_ptr(rows), n_seq * n_kv, T, d, _ptr(cache), cap, int(slot_offset),
+                                  _stream(stream))
+    L.check(st, "pgkq_pack_values")
+    return cache
+
+
+def pgkq_unpack_values(cache: torch.Tensor, n_tokens=None, slot_offset: int = 0, stream=None):
+    """Slots [slot_offset, slot_offset + n_tokens) of a tiled value cache -> rows
+    [n_seq, n_kv, n_tokens, d] fp16."""
+    n_seq, n_kv, cap, d = cache.shape
+    T = cap - int(slot_offset) if n_tokens is None else int(n_tokens)
+    rows = torch.empty((n_seq, n_kv, T, d), dtype=torch.float16, device=cache.device)
+    st = L.lib().pgkq_unpack_values(_ptr(cache), n_seq * n_kv, cap, d, int(slot_offset), T,
+                                    _ptr(rows), _stream(stream))
+    L.check(st, "pgkq_unpack_values")
+    return rows
+
+
 def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor, n_tokens=None,
                           softmax_scale: float = 0.0, n_splits: int = 0, out=None, workspace=None,
                           events=None, stream=None):
+    """K16 [n_seq, n_kv, cap, d] fp16 rows; V16 the tiled value cache of the same shape."""
     n_seq, n_q, d = q.shape
     n_kv, cap = K16.shape[1], K16.shape[2]
     n_tok = cap if n_tokens is None else int(n_tokens)
@@ -303,7 +334,8 @@ def pgkq_rtn_decode_workspace_bytes(head_dim, n_seq, n_q, n_kv, n_tokens, n_spli
 def pgkq_rtn_decode_attn(q: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, bits: int,
                          n_tokens=None, softmax_scale: float = 0.0, n_splits: int = 0, out=None,
                          workspace=None, events=None, stream=None):
-    """q [n_seq, n_q, d]; codes [n_seq, n_kv, cap * record]; V [n_seq, n_kv, cap, d] fp16."""
+    """q [n_seq, n_q, d]; codes [n_seq, n_kv, cap * record]; V the tiled fp16 value cache
+    [n_seq, n_kv, cap, d]."""
     n_seq, n_q, d = q.shape
     n_kv, cap = V.shape[1], V.shape[2]
     n_tok = cap if n_tokens is None else int(n_tokens)

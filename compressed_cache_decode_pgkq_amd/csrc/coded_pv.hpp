@@ -17,7 +17,7 @@
 // partial state (m, l, o[d], a[m]).
 #pragma once
 
-#include "softmax_pv.hpp"
+#include "device_common.hpp"
 
 namespace pgkq {
 

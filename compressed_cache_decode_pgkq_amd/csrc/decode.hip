@@ -132,7 +132,8 @@ __device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int
     uint16_t* nu = reinterpret_cast<uint16_t*>(base + size_t(4) * (NC + NSW) * a.capacity);
     nu[slot] = f64_to_f16_rne_sat_nonneg(sqrt(ss));
   }
-  if (tid < D) a.V_w[(size_t(stream) * a.capacity + slot) * D + tid] = a.v_new[size_t(stream) * D + tid];
+  if (tid < D)  // the value row goes into the stream's 32-token tiles
+    a.V_w[size_t(stream) * a.capacity * D + vtile_index(slot, tid, D)] = a.v_new[size_t(stream) * D + tid];
 }
 
 // ------------------------------------------------------------------ query prep

@@ -184,4 +184,33 @@ __device__ __forceinline__ uint16_t f64_to_f16_rne_sat_nonneg(double x) {
   return __half_as_ushort(__float2half_rn(f));
 }
 
+// G consecutive floats of LDS (vector reads for G = 2, 4, 8).
+template <int G>
+__device__ __forceinline__ void lds_fetch(const float* p, float (&v)[G]) {
+  if constexpr (G == 1) {
+    v[0] = p[0];
+  } else if constexpr (G == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(p);
+    v[0] = t.x;
+    v[1] = t.y;
+  } else {
+#pragma unroll
+    for (int k = 0; k < G; k += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(p + k);
+      v[k] = t.x;
+      v[k + 1] = t.y;
+      v[k + 2] = t.z;
+      v[k + 3] = t.w;
+    }
+  }
+}
+
+// Orders the LDS accesses of one wavefront around this point (wave-private
+// LDS rows written by some lanes and read by others).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 }  // namespace pgkq

@@ -11,9 +11,9 @@
 // its rows, sends the other half to a partner lane (DPP: xor 1, xor 2, the
 // half-row mirror, the 8-lane rotation) and adds what it receives.  After the
 // last level lane k holds the full scores of one row, which feed the shared
-// softmax and fp16 P.V tail.  Queries are applied as a log2-domain softmax
-// scale.
-#include "softmax_pv.hpp"
+// softmax and the matrix-core P.V tail (values in 32-token tiles).  Queries are
+// applied as a log2-domain softmax scale.
+#include "mfma_pv.hpp"
 
 namespace pgkq {
 
@@ -45,11 +45,14 @@ constexpr int fp16_min_waves() { return G * D > 512 ? 1 : 2; }
 template <int D, int G, bool WAVE_PARTS>
 __global__ void __launch_bounds__(kThreads, (fp16_min_waves<D, G>()))
 fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* __restrict__ V) {
-  using SM = SoftmaxPV<D, G, kWaves>;
-  constexpr int NIT = kWave / SM::TPI;  // rows per lane group per chunk (16 or 8)
+  using SM = MfmaPV<D, G, kWaves>;
+  constexpr int LPT = D / 8;            // lanes per key row
+  constexpr int TPI = kWave / LPT;      // key rows per wavefront load
+  constexpr int NIT = kWave / TPI;      // rows per lane group per chunk (16 or 8)
   constexpr int LEVELS = NIT == 16 ? 4 : 3;
   __shared__ __align__(16) float s_merge[SM::MERGE_FLOATS];
   __shared__ __align__(16) float s_p[kWaves][kWave][G];
+  static_assert(sizeof(s_p[0]) >= MfmaPV<D, G, kWaves>::P_BYTES, "weight rows");
 
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
@@ -58,7 +61,7 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
 
   SM sm;
   sm.init(tid);
-  const int lane = sm.lane, wave = sm.wave, k = sm.dblk, slot = sm.slot;
+  const int wave = sm.wave, k = sm.lane % LPT, slot = sm.lane / LPT;
 
   // this lane's 8 channels of every query head of the group
   float qr[G][8];
@@ -70,14 +73,15 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
 
   const int kb = keep_bits(k);
   const int my_row = kb & (NIT - 1);          // row of the chunk this lane ends up scoring
-  const int prow = my_row * SM::TPI + slot;   // its token index within the chunk
+  const int prow = my_row * TPI + slot;       // its token index within the chunk
 
   const int64_t t_begin = int64_t(split) * a.tokens_per_split;
   const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
-  const uint32_t range = static_cast<uint32_t>(t_end * D * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(K + size_t(stream) * a.capacity * D, range);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + size_t(stream) * a.capacity * D, range);
+  const __amdgpu_buffer_rsrc_t krs =
+      make_rsrc(K + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V + size_t(stream) * a.capacity * D,
+                                               static_cast<uint32_t>((t_end + 31) / 32 * 32 * D * 2));
 
   int64_t c_first, c_end, c_step;
   if constexpr (WAVE_PARTS) {
@@ -101,8 +105,8 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
     typename SM::VChunk vc;
     u32x4 kr[KROWS];
 #pragma unroll
-    for (int r = 0; r < KROWS; ++r) kr[r] = buf_load_b128(krs, kbase + r * SM::TPI * D * 2);
-    if constexpr (!kSplitK) sm.load_v(vc, c0, vrs);
+    for (int r = 0; r < KROWS; ++r) kr[r] = buf_load_b128(krs, kbase + r * TPI * D * 2);
+    if constexpr (!kSplitK) sm.load_v(vc, c0, vrs, t_end);
 
     // partial dot products of row `it` (8 channels), reduced level by level as
     // soon as both halves of a level exist: at most LEVELS + 1 live per head
@@ -114,7 +118,7 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
         sched_fence();
 #pragma unroll
         for (int r = 0; r < KROWS; ++r)
-          kr[r] = buf_load_b128(krs, kbase + (KROWS + r) * SM::TPI * D * 2);
+          kr[r] = buf_load_b128(krs, kbase + (KROWS + r) * TPI * D * 2);
       }
       __half2 hk[4];
       __builtin_memcpy(hk, &kr[it % KROWS], sizeof(hk));
@@ -154,7 +158,7 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
     }
     if constexpr (kSplitK) {
       sched_fence();  // keep the value loads behind the key registers' last use
-      sm.load_v(vc, c0, vrs);
+      sm.load_v(vc, c0, vrs, t_end);
     }
     const bool valid = c0 + prow < c_end;
     sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], prow);

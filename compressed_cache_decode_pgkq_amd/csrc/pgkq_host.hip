@@ -61,6 +61,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // The scans address one stream's codes and value rows through buffer
 // resources with 32-bit byte ranges and offsets.
 constexpr size_t kMaxStreamBytes = 0xFFFFFFF0u;
+// fp16 value caches are stored in 32-token tiles: their capacity is a
+// multiple of the tile.
+constexpr int64_t kValueTile = 32;
+
 bool fits_buffer(int64_t capacity, size_t record_bytes, int d) {
   return size_t(capacity) * record_bytes <= kMaxStreamBytes &&
          size_t(capacity) * size_t(d) * 2 <= kMaxStreamBytes;
@@ -487,6 +491,7 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
   if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
   if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;
+  if (!logits_mode && capacity % kValueTile) return PGKQ_ERR_SHAPE;
   if (!fits_buffer(capacity, g.record_bytes(), g.d)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
       !aligned16(workspace) || (perm && !aligned16(perm)) || (S && !aligned16(S)) ||
@@ -714,6 +719,43 @@ size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t
   return fp16_ws(head_dim, n_seq, n_q, sp);
 }
 
+static pgkq_status values_common(const void* src, void* dst, int64_t n_streams, int64_t n_tokens,
+                                 int32_t head_dim, int64_t capacity, int64_t slot_offset,
+                                 bool unpack, void* stream) {
+  if (head_dim < 16 || head_dim > 1024 || head_dim % 16) return PGKQ_ERR_UNSUPPORTED;
+  if (n_streams < 0 || n_tokens < 0 || slot_offset < 0 || capacity < 0) return PGKQ_ERR_SHAPE;
+  if (capacity % kValueTile || slot_offset + n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (size_t(capacity) * size_t(head_dim) * 2 > kMaxStreamBytes) return PGKQ_ERR_SHAPE;
+  if (n_streams == 0 || n_tokens == 0) return PGKQ_OK;  // nothing to move
+  if (!src || !dst) return PGKQ_ERR_NULL;
+  if (!aligned16(unpack ? src : dst) || (reinterpret_cast<uintptr_t>(unpack ? dst : src) & 1u))
+    return PGKQ_ERR_ALIGN;
+  pgkq::ValuesArgs a{};
+  a.src = static_cast<const __half*>(src);
+  a.dst = static_cast<__half*>(dst);
+  a.n_streams = n_streams;
+  a.n_tokens = n_tokens;
+  a.capacity = capacity;
+  a.slot_offset = slot_offset;
+  a.d = head_dim;
+  a.unpack = unpack;
+  return pgkq::launch_values(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PGKQ_OK
+                                                                               : PGKQ_ERR_HIP;
+}
+
+pgkq_status pgkq_pack_values(const void* rows, int64_t n_streams, int64_t n_tokens, int32_t head_dim,
+                             void* cache, int64_t capacity, int64_t slot_offset, void* stream) {
+  return values_common(rows, cache, n_streams, n_tokens, head_dim, capacity, slot_offset, false,
+                       stream);
+}
+
+pgkq_status pgkq_unpack_values(const void* cache, int64_t n_streams, int64_t capacity,
+                               int32_t head_dim, int64_t slot_offset, int64_t n_tokens, void* rows,
+                               void* stream) {
+  return values_common(cache, rows, n_streams, n_tokens, head_dim, capacity, slot_offset, true,
+                       stream);
+}
+
 pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q,
                                   int64_t n_kv, int64_t n_tokens, int64_t capacity,
                                   int32_t head_dim, const void* K16, const void* V16, float* out,
@@ -727,6 +769,7 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   int group = 0;
   if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
   if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (capacity % kValueTile) return PGKQ_ERR_SHAPE;
   if (!fits_buffer(capacity, 0, head_dim)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(K16) || !aligned16(V16) || !aligned16(out) ||
       (workspace && !aligned16(workspace)))
@@ -831,6 +874,7 @@ static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void*
   int group = 0;
   if ((st = check_group(n_q, n_kv, &group)) != PGKQ_OK) return st;
   if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
+  if (!logits_mode && capacity % kValueTile) return PGKQ_ERR_SHAPE;
   if (!fits_buffer(capacity, rtn_record(head_dim, bits), head_dim)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(codes) || !aligned16(workspace) || (V && !aligned16(V)) ||
       (out && !aligned16(out)) || (logits && !aligned16(logits)))

@@ -151,6 +151,19 @@ struct RtnDecodeArgs {
   float scale_log2;
 };
 
+// fp16 value rows <-> the 32-token-tile value cache
+struct ValuesArgs {
+  const __half* src;
+  __half* dst;
+  int64_t n_streams;
+  int64_t n_tokens;
+  int64_t capacity;
+  int64_t slot_offset;
+  int d;
+  bool unpack;  // false: rows -> cache, true: cache -> rows
+};
+
+hipError_t launch_values(const ValuesArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_encode(const Geometry& g, const EncodeArgs& a, hipStream_t s);
 hipError_t launch_query_prep(const Geometry& g, const DecodeArgs& a, hipStream_t s);

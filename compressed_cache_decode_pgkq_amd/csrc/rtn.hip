@@ -21,7 +21,7 @@
 //                   lane = token for the score, the query read through the
 //                   scalar cache (wave-uniform), then the shared online softmax
 //                   and fp16 P.V tail.
-#include "softmax_pv.hpp"
+#include "mfma_pv.hpp"
 
 namespace pgkq {
 
@@ -191,9 +191,10 @@ __global__ void __launch_bounds__(kThreads, 2)
 rtn_scan_kernel(RtnDecodeArgs a, const uint8_t* __restrict__ codes, const __half* __restrict__ V) {
   constexpr int NC = D * BITS / 32;
   constexpr int NW = NC + 1;
-  constexpr int MERGE_FLOATS = SoftmaxPV<D, G, kWaves>::MERGE_FLOATS;
+  constexpr int MERGE_FLOATS = MfmaPV<D, G, kWaves>::MERGE_FLOATS;
   __shared__ __align__(16) float s_merge[MERGE_FLOATS];
   __shared__ __align__(16) float s_p[kWaves][kWave][G];
+  static_assert(sizeof(s_p[0]) >= MfmaPV<D, G, kWaves>::P_BYTES, "weight rows");
 
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
@@ -207,10 +208,10 @@ rtn_scan_kernel(RtnDecodeArgs a, const uint8_t* __restrict__ codes, const __half
   const __amdgpu_buffer_rsrc_t crs =
       make_rsrc(codes + size_t(stream) * a.stream_bytes, static_cast<uint32_t>(a.stream_bytes));
   const __amdgpu_buffer_rsrc_t vrs =
-      make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
+      make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>((t_end + 31) / 32 * 32 * D * 2));
   const uint32_t row_bytes = 4u * static_cast<uint32_t>(a.capacity);
 
-  SoftmaxPV<D, G, kWaves> sm;
+  MfmaPV<D, G, kWaves> sm;
   sm.init(tid);
   const int lane = sm.lane, wave = sm.wave;
 
@@ -234,8 +235,8 @@ rtn_scan_kernel(RtnDecodeArgs a, const uint8_t* __restrict__ codes, const __half
     const uint32_t t4 = static_cast<uint32_t>(t) * 4u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) cw[w] = buf_load_b32(crs, t4 + w * row_bytes);
-    typename SoftmaxPV<D, G, kWaves>::VChunk vc;
-    if constexpr (!LOGITS) sm.load_v(vc, c0, vrs);
+    typename MfmaPV<D, G, kWaves>::VChunk vc;
+    if constexpr (!LOGITS) sm.load_v(vc, c0, vrs, t_end);
 
     float acc[G];
 #pragma unroll

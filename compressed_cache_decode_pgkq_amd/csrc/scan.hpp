@@ -9,13 +9,14 @@
 // tables of signed nibble sums of kappa * S_h q~ for the sketch.  Lane = token
 // for the score: one coalesced dword load per code word, one LDS read per pair
 // giving all G heads, one per sketch nibble.  The value path (template VB):
-// VB = 0 reads fp16 value rows (SoftmaxPV), VB > 0 reads values coded with
-// b_main = VB (CodedPV).
+// VB = 0 reads fp16 values in 32-token tiles and sums them on the matrix cores
+// (MfmaPV), VB > 0 reads values coded with b_main = VB (CodedPV).
 #pragma once
 
 #include <type_traits>
 
 #include "coded_pv.hpp"
+#include "mfma_pv.hpp"
 
 namespace pgkq {
 
@@ -59,7 +60,7 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* cw, int i) {
 
 template <int D, int G, int VB, bool QJL>
 using ValuePath = std::conditional_t<(VB > 0), CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>,
-                                     SoftmaxPV<D, G, kScanWaves>>;
+                                     MfmaPV<D, G, kScanWaves>>;
 
 template <int D, int BM, bool QJL, int G, bool LOGITS, int VB = 0>
 __global__ void __launch_bounds__(kScanThreads, kScanMinWavesPerEU)
@@ -80,6 +81,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   __shared__ __align__(16) float s_tab[MAIN_FLOATS];
   __shared__ __align__(16) float s_qt[NQT];
   __shared__ __align__(16) float s_p[kScanWaves][kWave][G];
+  static_assert(CODED_V || sizeof(s_p[0]) >= MfmaPV<D, G, kScanWaves>::P_BYTES, "weight rows");
   // coded values: per-wavefront transposition blocks and the pair table
   constexpr int VW_WORDS = CODED_V ? CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>::LDS_WORDS : 1;
   constexpr int VTAB = CODED_V ? (1 << (2 * VB - 1)) : 1;
@@ -104,7 +106,8 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   const __amdgpu_buffer_rsrc_t vrs =
       CODED_V ? make_rsrc(a.codes_v + size_t(stream) * a.stream_bytes_v,
                           static_cast<uint32_t>(a.stream_bytes_v))
-              : make_rsrc(V + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
+              : make_rsrc(V + size_t(stream) * a.capacity * D,
+                          static_cast<uint32_t>((t_end + 31) / 32 * 32 * D * 2));
   const uint32_t nu_off = 4u * NW * static_cast<uint32_t>(a.capacity);
   const uint32_t row_bytes = 4u * static_cast<uint32_t>(a.capacity);
 
@@ -200,7 +203,13 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     const int64_t t = c0 + lane;
     const bool valid = t < c_end;
     load_codes(c0);
-    if constexpr (!LOGITS) sm.load_v(vc, c0, vrs);
+    if constexpr (!LOGITS) {
+      if constexpr (CODED_V) {
+        sm.load_v(vc, c0, vrs);
+      } else {
+        sm.load_v(vc, c0, vrs, t_end);
+      }
+    }
 
     float s[G];
 #pragma unroll

@@ -31,6 +31,15 @@
  *    larger capacities are rejected with PGKQ_ERR_SHAPE.
  *  - n_tokens == 0 is a valid no-op (outputs untouched, except that decode
  *    attention writes zeros to `out` because an empty softmax has no weights).
+ *  - fp16 value caches ("V" below) are stored in 32-TOKEN TILES, the operand
+ *    order of the matrix-core weighted sum: stream (b, h) holds `capacity`
+ *    slots (capacity a multiple of 32, else PGKQ_ERR_SHAPE), and element
+ *    (t, c) of it sits at half-word
+ *      (t/32) 32 d + ((c/16) 4 + (t%32)/8) 128 + (c%16) 8 + t%8
+ *    (16 contiguous bytes hold 8 consecutive tokens of one channel).  Streams
+ *    lie back to back in [n_seq][n_kv] order, capacity * d half-words each.
+ *    pgkq_pack_values / pgkq_unpack_values convert from / to plain rows.  Slots
+ *    at or beyond n_tokens may hold any bits; they are never weighted.
  *
  * Code layout of one (sequence, kv-head) stream with room for `capacity` tokens
  * (exactly pgkq_record_bytes() bytes per token slot):
@@ -171,8 +180,11 @@ size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t 
  *   q     [n_seq][n_q][d], dtype q_dtype (F32, F16 or BF16); query head hq reads
  *         kv-head hq / (n_q / n_kv); n_q / n_kv must be 1, 2, 4 or 8
  *   codes as written by pgkq_encode, tokens [0, n_tokens) of each stream
- *   V     [n_seq][n_kv][capacity][d] fp16
+ *   V     fp16 value cache in 32-token tiles (n_seq * n_kv streams of
+ *         `capacity` slots, see the conventions above)
  *   out   [n_seq][n_q][d] fp32 = sum_t softmax_t(scale * logit_t) V_t
+ * The weighted sum runs on the matrix cores with the softmax weights rounded
+ * to fp16 (fp32 accumulation); the denominator sums the same rounded weights.
  *   softmax_scale <= 0 selects 1 / sqrt(d).
  * The logit of token t is
  *   sum_i level[rc_i] (q~[2i] cos thetahat[ac_i] + q~[2i+1] sin thetahat[ac_i])
@@ -191,7 +203,7 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
 /* One decode step of a live cache: append the new token, then attend over it.
  * Encodes k_new [n_seq][n_kv][d] (k_dtype F32 or F16; steps (1)-(4), one key per
  * stream) into slot n_cached of every stream of `codes`, copies v_new
- * [n_seq][n_kv][d] fp16 into slot n_cached of V, then computes decode attention
+ * [n_seq][n_kv][d] fp16 into slot n_cached of the tiled V, then computes decode attention
  * over tokens [0, n_cached] exactly as pgkq_decode_attn with n_tokens =
  * n_cached + 1.  The append runs inside the query-preparation launch (no
  * extra kernel); its decisions are taken in float64 on the unnormalized
@@ -216,6 +228,24 @@ pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype
                                  float* logits, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* Write fp16 value rows into the 32-token-tile value cache (layout in the
+ * conventions above):
+ *   rows   [n_streams][n_tokens][head_dim] fp16, plain rows (2-byte aligned)
+ *   cache  n_streams streams of `capacity` slots (16-byte aligned);
+ *          slots [slot_offset, slot_offset + n_tokens) are written, every
+ *          other slot keeps its contents.
+ * head_dim a multiple of 16 up to 1024; capacity a multiple of 32;
+ * slot_offset + n_tokens <= capacity.  n_streams or n_tokens == 0 is a no-op
+ * (the pointers may then be NULL).  One kernel, no workspace. */
+pgkq_status pgkq_pack_values(const void* rows, int64_t n_streams, int64_t n_tokens, int32_t head_dim,
+                             void* cache, int64_t capacity, int64_t slot_offset, void* stream);
+
+/* The inverse: slots [slot_offset, slot_offset + n_tokens) of every stream of
+ * the tiled cache into rows [n_streams][n_tokens][head_dim]. */
+pgkq_status pgkq_unpack_values(const void* cache, int64_t n_streams, int64_t capacity,
+                               int32_t head_dim, int64_t slot_offset, int64_t n_tokens, void* rows,
+                               void* stream);
+
 /* Bytes of workspace pgkq_fp16_decode_attn needs. */
 size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q,
                                         int64_t n_kv, int64_t n_tokens,
@@ -223,7 +253,8 @@ size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t
 
 /* Uncompressed comparator: decode attention on an fp16 key cache (the FP16
  * cache the pages take fidelity deltas against).
- *   K16, V16 [n_seq][n_kv][capacity][d] fp16; q, out, scale as for decode. */
+ *   K16 [n_seq][n_kv][capacity][d] fp16 rows; V16 the fp16 value cache in
+ *   32-token tiles (as for decode); q, out, scale as for decode. */
 pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q,
                                   int64_t n_kv, int64_t n_tokens, int64_t capacity,
                                   int32_t head_dim, const void* K16, const void* V16, float* out,

@@ -44,6 +44,40 @@ def k_tensor(K):
     return torch.from_numpy(np.ascontiguousarray(K)).to(DEV)
 
 
+VALUE_TILE = 32
+
+
+def value_capacity(T: int) -> int:
+    """Smallest value-cache capacity holding T tokens (a multiple of the 32-token tile)."""
+    return max(VALUE_TILE, -(-T // VALUE_TILE) * VALUE_TILE)
+
+
+def tile_values(V, cap):
+    """Rows V [n_seq, n_kv, T, d] -> an [n_seq, n_kv, cap, d] fp16 array whose memory is the
+    32-token-tile value cache: element (t, c) at half-word
+    (t/32) 32 d + ((c/16) 4 + (t%32)/8) 128 + (c%16) 8 + t%8 of its stream.
+    Slots past T are zero."""
+    n_seq, n_kv, T, d = V.shape
+    buf = np.zeros((n_seq, n_kv, cap, d), dtype=np.float16)
+    buf[:, :, :T] = V
+    # t = 32 a + 8 b + e, c = 16 f + g  ->  order (a, f, b, g, e)
+    x = buf.reshape(n_seq, n_kv, cap // 32, 4, 8, d // 16, 16).transpose(0, 1, 2, 5, 3, 6, 4)
+    return np.ascontiguousarray(x).reshape(n_seq, n_kv, cap, d)
+
+
+def untile_values(buf, T=None):
+    """Inverse of tile_values: the tiled cache (array of shape [n_seq, n_kv, cap, d]) -> rows."""
+    n_seq, n_kv, cap, d = buf.shape
+    x = np.asarray(buf).reshape(n_seq, n_kv, cap // 32, d // 16, 4, 16, 8).transpose(0, 1, 2, 4, 6, 3, 5)
+    rows = np.ascontiguousarray(x).reshape(n_seq, n_kv, cap, d)
+    return rows if T is None else rows[:, :, :T]
+
+
+def v_cache(V, cap):
+    """Device copy of the tiled value cache of rows V."""
+    return to_dev(tile_values(np.asarray(V, dtype=np.float16), cap))
+
+
 class Case:
     """Oracle-side encoding of a workload plus its device copies."""
 
@@ -54,7 +88,7 @@ class Case:
         inp = inputs if inputs is not None else make_inputs(cfg)
         T = cfg.n_tokens if n_tokens is None else n_tokens
         self.T = T
-        self.cap = capacity if capacity is not None else max(T, 2) + (max(T, 2) & 1)
+        self.cap = capacity if capacity is not None else value_capacity(T)
         self.K = inp["K"][:, :, :T]
         self.V = inp["V"][:, :, :T]
         self.q = inp["q"]
@@ -91,12 +125,10 @@ class Case:
     def dev_inputs(self):
         cap = self.cap
         n_seq, n_kv, _, d = self.K.shape
-        Vpad = np.zeros((n_seq, n_kv, cap, d), dtype=np.float16)
-        Vpad[:, :, : self.T] = self.V
         return dict(
             signs=to_dev(self.signs),
             perm=to_dev(self.perm.astype(np.uint16).view(np.int16)) if self.perm_arg is not None else None,
             codebook=to_dev(self.cb),
             S=to_dev(self.S) if self.S is not None else None,
-            V=to_dev(Vpad),
+            V=v_cache(self.V, cap),
         )

@@ -333,3 +333,46 @@ def test_decode_step_validation():
     assert call(k=MIS) == L.PGKQ_ERR_ALIGN
     assert call(v=MIS) == L.PGKQ_ERR_ALIGN
     assert call(wsb=16) == L.PGKQ_ERR_WORKSPACE
+
+
+def test_value_cache_capacity_must_be_a_tile_multiple():
+    """fp16 value caches come in 32-token tiles: every entry point that reads one
+    rejects a capacity that is not a multiple of 32 (even ones included)."""
+    assert _decode(cap=144, n_tok=100) == L.PGKQ_ERR_SHAPE
+    assert _rtn_decode(cap=144) == L.PGKQ_ERR_SHAPE
+    o = L.PgkqLaunchOpts(0, None, None)
+    st = L.lib().pgkq_fp16_decode_attn(_vp(A), L.PGKQ_F32, 1, 4, 4, 10, 48, 64, _vp(A), _vp(A),
+                                       _vp(A), 0.0, ctypes.byref(o), _vp(A), 1 << 20, None)
+    assert st == L.PGKQ_ERR_SHAPE
+    st = L.lib().pgkq_decode_step(_params(128, 3, 2, 128, 1), _vp(A), L.PGKQ_BF16, _vp(A), L.PGKQ_F16,
+                                  _vp(A), 2, 8, 2, 99, 144, _vp(A), None, _vp(A), _vp(A), _vp(A),
+                                  _vp(A), _vp(A), 0.0, ctypes.byref(o), _vp(A), 1 << 30, None)
+    assert st == L.PGKQ_ERR_SHAPE
+
+
+def test_pack_values_validation():
+    lib = L.lib()
+
+    def pack(rows=A, n_streams=4, T=50, d=128, cache=A, cap=64, off=0):
+        return lib.pgkq_pack_values(_vp(rows) if rows else None, n_streams, T, d,
+                                    _vp(cache) if cache else None, cap, off, None)
+
+    def unpack(cache=A, n_streams=4, cap=64, d=128, off=0, T=50, rows=A):
+        return lib.pgkq_unpack_values(_vp(cache) if cache else None, n_streams, cap, d, off, T,
+                                      _vp(rows) if rows else None, None)
+
+    for f in (pack, unpack):
+        assert f(d=8) == L.PGKQ_ERR_UNSUPPORTED
+        assert f(d=72) == L.PGKQ_ERR_UNSUPPORTED
+        assert f(d=2048) == L.PGKQ_ERR_UNSUPPORTED
+        assert f(cap=48) == L.PGKQ_ERR_SHAPE
+        assert f(off=20) == L.PGKQ_ERR_SHAPE          # 20 + 50 > 64
+        assert f(T=-1) == L.PGKQ_ERR_SHAPE
+        assert f(n_streams=-1) == L.PGKQ_ERR_SHAPE
+        assert f(cap=1 << 24) == L.PGKQ_ERR_SHAPE     # stream beyond the 32-bit buffer range
+        assert f(rows=0) == L.PGKQ_ERR_NULL
+        assert f(cache=0) == L.PGKQ_ERR_NULL
+        assert f(T=0, rows=0, cache=0) == L.PGKQ_OK    # empty: nothing to move
+        assert f(n_streams=0, rows=0, cache=0) == L.PGKQ_OK
+        assert f(cache=MIS) == L.PGKQ_ERR_ALIGN       # the tiled side moves 16-byte pieces
+        assert f(rows=A + 1) == L.PGKQ_ERR_ALIGN      # fp16 rows: 2-byte aligned

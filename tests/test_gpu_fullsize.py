@@ -10,7 +10,7 @@ import torch
 from oracle import attn, calibrate, codebook, encode, layout
 from synth import CONFIGS, make_inputs
 
-from gpu_cases import k_tensor, lib_params, params_of, q_tensor, to_dev
+from gpu_cases import k_tensor, lib_params, params_of, q_tensor, to_dev, untile_values, v_cache
 from parity_util import assert_code_parity, classify, codebook_array, merge_counts
 
 pytestmark = pytest.mark.gpu
@@ -65,8 +65,8 @@ def _run_full(cfg, samples, n_splits):
         inp.setdefault("fields", {})[(b, h)] = f
     print(cfg.name, "encode", counts)
     assert_code_parity(counts)
-    out = api.pgkq_decode_attn(lp, q_tensor(q, cfg.q_dtype), codes, to_dev(V), dsigns, None, dcb, dS,
-                               n_splits=n_splits)
+    out = api.pgkq_decode_attn(lp, q_tensor(q, cfg.q_dtype), codes, v_cache(V, cap), dsigns, None, dcb,
+                               dS, n_splits=n_splits)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     G = cfg.n_q // cfg.n_kv
@@ -132,7 +132,8 @@ def test_c2_fp16_comparator_full_size():
     cfg = CONFIGS["nano_b64_t512"]
     inp = make_inputs(cfg)
     K16 = inp["K"].astype(np.float16)
-    out = api.pgkq_fp16_decode_attn(q_tensor(inp["q"], cfg.q_dtype), to_dev(K16), to_dev(inp["V"]))
+    out = api.pgkq_fp16_decode_attn(q_tensor(inp["q"], cfg.q_dtype), to_dev(K16),
+                                    v_cache(inp["V"], cfg.n_tokens))
     torch.cuda.synchronize()
     out = out.cpu().numpy()
     worst = 0.0
@@ -160,7 +161,7 @@ def test_c3_rtn_control_full_size_sampled(bits):
     cfg, inp = _c3_inputs()
     K, V, q = inp["K"], inp["V"], inp["q"]
     codes = api.pgkq_rtn_encode(k_tensor(K), bits)
-    out = api.pgkq_rtn_decode_attn(q_tensor(q, cfg.q_dtype), codes, to_dev(V), bits,
+    out = api.pgkq_rtn_decode_attn(q_tensor(q, cfg.q_dtype), codes, v_cache(V, cfg.n_tokens), bits,
                                    n_splits=cfg.n_splits)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
@@ -183,7 +184,7 @@ def test_c3_fp16_comparator_full_size_sampled():
     api = _api()
     cfg, inp = _c3_inputs()
     K16, V, q = inp["K"].astype(np.float16), inp["V"], inp["q"]
-    out = api.pgkq_fp16_decode_attn(q_tensor(q, cfg.q_dtype), to_dev(K16), to_dev(V),
+    out = api.pgkq_fp16_decode_attn(q_tensor(q, cfg.q_dtype), to_dev(K16), v_cache(V, cfg.n_tokens),
                                     n_splits=cfg.n_splits)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
@@ -260,15 +261,17 @@ def test_c3_decode_step_full_size_sampled():
     dsigns, dcb, dS = to_dev(signs), to_dev(codebook_array(tables)), to_dev(S)
     codes = api.pgkq_encode(lib_params(p), k_tensor(K[:, :, :T - 1]), dsigns, None, dcb, dS,
                             capacity=cap)
-    Vd = to_dev(V)
-    Vd[:, :, T - 1] = 0
+    Vz = V.copy()
+    Vz[:, :, T - 1] = 0
+    Vd = v_cache(Vz, cap)
+    del Vz
     out = api.pgkq_decode_step(lib_params(p), q_tensor(q, cfg.q_dtype),
                                k_tensor(np.ascontiguousarray(K[:, :, T - 1])),
                                to_dev(np.ascontiguousarray(V[:, :, T - 1])), codes, Vd, T - 1,
                                dsigns, None, dcb, dS, n_splits=cfg.n_splits)
     torch.cuda.synchronize()
     out = out.cpu().numpy()
-    assert torch.equal(Vd.cpu(), torch.from_numpy(V))
+    assert np.array_equal(untile_values(Vd.cpu().numpy()), V)
     G = cfg.n_q // cfg.n_kv
     counts, worst = {}, 0.0
     for (b, h) in [(0, 0), (15, 7)]:

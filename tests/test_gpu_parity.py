@@ -16,7 +16,7 @@ import torch
 from oracle import attn, layout
 from synth import CONFIGS
 
-from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev
+from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev, v_cache, value_capacity
 from parity_util import assert_code_parity, classify, merge_counts
 
 pytestmark = pytest.mark.gpu
@@ -240,16 +240,14 @@ def _fp16_check(cfg, n_splits=0, T=None, cap=None):
     api = _api()
     inp = make_inputs(cfg)
     T = cfg.n_tokens if T is None else T
-    cap = T if cap is None else cap
+    cap = value_capacity(T) if cap is None else cap
     n_seq, n_kv = cfg.n_seq, cfg.n_kv
     d = cfg.head_dim
     K16 = inp["K"][:, :, :T].astype(np.float16)
     V16 = inp["V"][:, :, :T]
     Kp = np.zeros((n_seq, n_kv, cap, d), np.float16)
-    Vp = np.zeros((n_seq, n_kv, cap, d), np.float16)
     Kp[:, :, :T] = K16
-    Vp[:, :, :T] = V16
-    out = api.pgkq_fp16_decode_attn(q_tensor(inp["q"], cfg.q_dtype), to_dev(Kp), to_dev(Vp),
+    out = api.pgkq_fp16_decode_attn(q_tensor(inp["q"], cfg.q_dtype), to_dev(Kp), v_cache(V16, cap),
                                     n_tokens=T, n_splits=n_splits)
     torch.cuda.synchronize()
     ref, _ = attn.fp16_attention(inp["q"], K16, V16)

@@ -16,7 +16,7 @@ import torch
 from oracle import rtn
 from synth import CONFIGS, make_inputs
 
-from gpu_cases import k_tensor, q_tensor, to_dev
+from gpu_cases import k_tensor, q_tensor, to_dev, v_cache, value_capacity
 
 pytestmark = pytest.mark.gpu
 
@@ -121,13 +121,10 @@ def _check_decode(K, V, q, q_dtype, bits, n_splits=0, T=None, cap=None):
     """GPU decode on the oracle's packed records vs the oracle decode."""
     api = _api()
     T = K.shape[2] if T is None else T
-    cap = max(T, 1) if cap is None else cap
-    n_seq, n_kv, _, d = K.shape
+    cap = value_capacity(T) if cap is None else cap
     K = K[:, :, :T].astype(np.float64)
     recs = rtn.pack_cache(K, bits, cap)
-    Vpad = np.zeros((n_seq, n_kv, cap, d), dtype=np.float16)
-    Vpad[:, :, :T] = V[:, :, :T]
-    out = api.pgkq_rtn_decode_attn(q_tensor(q, q_dtype), to_dev(recs), to_dev(Vpad), bits,
+    out = api.pgkq_rtn_decode_attn(q_tensor(q, q_dtype), to_dev(recs), v_cache(V[:, :, :T], cap), bits,
                                    n_tokens=T, n_splits=n_splits)
     torch.cuda.synchronize()
     want = _oracle_out(q, K, V[:, :, :T], bits)
@@ -198,8 +195,8 @@ def test_rtn_long_stream_wave_partitions():
 def test_rtn_empty_cache_gives_zeros():
     api = _api()
     out = torch.full((1, 4, 64), 7.0, device="cuda:0")
-    recs = torch.zeros((1, 4, 16 * 36), dtype=torch.uint8, device="cuda:0")
-    V = torch.zeros((1, 4, 16, 64), dtype=torch.float16, device="cuda:0")
+    recs = torch.zeros((1, 4, 32 * 36), dtype=torch.uint8, device="cuda:0")
+    V = torch.zeros((1, 4, 32, 64), dtype=torch.float16, device="cuda:0")
     q = torch.ones((1, 4, 64), dtype=torch.float32, device="cuda:0")
     api.pgkq_rtn_decode_attn(q, recs, V, 4, n_tokens=0, out=out)
     torch.cuda.synchronize()
@@ -242,8 +239,10 @@ def test_rtn_end_to_end_encode_then_decode():
     api = _api()
     cfg, inp = _inputs("gqa_b16_t32k", n_seq=2, n_tokens=1000)
     K, V, q = inp["K"], inp["V"], inp["q"]
-    recs = _gpu_records(K, 3, K.shape[2])
-    out = api.pgkq_rtn_decode_attn(q_tensor(q, cfg.q_dtype), recs, to_dev(V), 3)
+    cap = value_capacity(K.shape[2])
+    recs = _gpu_records(K, 3, cap)
+    out = api.pgkq_rtn_decode_attn(q_tensor(q, cfg.q_dtype), recs, v_cache(V, cap), 3,
+                                   n_tokens=K.shape[2])
     torch.cuda.synchronize()
     want = _oracle_out(q, K.astype(np.float64), V, 3)
     assert float(np.abs(out.cpu().numpy() - want).max()) <= OUT_TOL

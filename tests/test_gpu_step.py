@@ -19,7 +19,7 @@ import torch
 from oracle import attn, layout
 from synth import CONFIGS
 
-from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev
+from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev, untile_values, v_cache, value_capacity
 from parity_util import assert_code_parity, classify, merge_counts
 
 pytestmark = pytest.mark.gpu
@@ -78,7 +78,7 @@ STEP_CASES = {
 def test_decode_step_appends_then_attends(name):
     cfg, kw = STEP_CASES[name]
     api = _api()
-    case = Case(cfg, capacity=cfg.n_tokens + 4, **kw)
+    case = Case(cfg, capacity=value_capacity(cfg.n_tokens + 1), **kw)
     T = case.T
     dev = case.dev_inputs()
     p = lib_params(case.p)
@@ -87,8 +87,9 @@ def test_decode_step_appends_then_attends(name):
                         device="cuda:0")
     api.pgkq_encode(p, k_tensor(case.K[:, :, :T - 1]), dev["signs"], dev["perm"], dev["codebook"],
                     dev["S"], codes=codes, capacity=case.cap)
-    Vd = dev["V"].clone()
-    Vd[:, :, T - 1:] = 0
+    Vz = case.V.copy()
+    Vz[:, :, T - 1:] = 0
+    Vd = v_cache(Vz, case.cap)
     k_new = k_tensor(np.ascontiguousarray(case.K[:, :, T - 1]))
     v_new = to_dev(np.ascontiguousarray(case.V[:, :, T - 1]))
     out = api.pgkq_decode_step(p, q_tensor(case.q, cfg.q_dtype), k_new, v_new, codes, Vd, T - 1,
@@ -98,8 +99,9 @@ def test_decode_step_appends_then_attends(name):
     counts = _counts(case, got, T)
     print(name, counts)
     assert_code_parity(counts)
-    assert torch.equal(Vd[:, :, T - 1].cpu(), v_new.cpu())
-    assert not Vd[:, :, T:].any()                      # nothing beyond the slot
+    rows = untile_values(Vd.cpu().numpy())
+    assert np.array_equal(rows[:, :, T - 1], v_new.cpu().numpy())
+    assert not rows[:, :, T:].any()                    # nothing beyond the slot
     err = float(np.abs(out.cpu().numpy() - _oracle_out(case, T)).max())
     assert err <= OUT_TOL, err
 
@@ -118,8 +120,9 @@ def test_decode_step_loop_matches_oracle_every_step():
                         device="cuda:0")
     api.pgkq_encode(p, k_tensor(case.K[:, :, :T0]), dev["signs"], dev["perm"], dev["codebook"],
                     dev["S"], codes=codes, capacity=case.cap)
-    Vd = dev["V"].clone()
-    Vd[:, :, T0:] = 0
+    Vz = case.V.copy()
+    Vz[:, :, T0:] = 0
+    Vd = v_cache(Vz, case.cap)
     q = q_tensor(case.q, cfg.q_dtype)
     for i, t in enumerate(range(T0, case.T)):
         out = api.pgkq_decode_step(p, q, k_tensor(np.ascontiguousarray(case.K[:, :, t])),
@@ -137,7 +140,7 @@ def test_decode_step_equals_encode_then_decode_when_codes_agree():
     the output of pgkq_encode + pgkq_decode_attn on the same cache, bit for bit."""
     api = _api()
     cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=333)
-    case = Case(cfg, capacity=336)
+    case = Case(cfg, capacity=352)
     dev = case.dev_inputs()
     p = lib_params(case.p)
     n_seq, n_kv, T, d = case.K.shape
