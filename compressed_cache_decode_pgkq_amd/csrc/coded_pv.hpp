@@ -174,31 +174,6 @@ struct CodedPV {
     }
   }
 
-  // Partial state of this wavefront as partial `pidx` of `n_parts` for query
-  // heads row0 .. row0 + G - 1.
-  __device__ __forceinline__ void finish_wave(float* __restrict__ partial, size_t row0, int pidx,
-                                              int n_parts) {
-    reduce_slots();
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float l_w = wave_sum(l_lane[g]);
-      float* part = partial + ((row0 + g) * n_parts + pidx) * WIDTH;
-      if (lane < LPT) {
-        *reinterpret_cast<float4*>(part + 4 + dblk * 8) = make_float4(o[g][0], o[g][1], o[g][2], o[g][3]);
-        *reinterpret_cast<float4*>(part + 8 + dblk * 8) = make_float4(o[g][4], o[g][5], o[g][6], o[g][7]);
-        float a[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) a[k] = QJLV ? 2.f * acc[g][k] - spn[g] : 0.f;
-        *reinterpret_cast<float4*>(part + 4 + D + dblk * 8) = make_float4(a[0], a[1], a[2], a[3]);
-        *reinterpret_cast<float4*>(part + 8 + D + dblk * 8) = make_float4(a[4], a[5], a[6], a[7]);
-      }
-      if (lane == 0) {
-        part[0] = m_run[g];
-        part[1] = l_w;
-      }
-    }
-  }
-
   static constexpr int MERGE_FLOATS = WAVES * G * (2 * D + 2);
 
   // The wavefronts of the workgroup merged through `scratch` (MERGE_FLOATS

@@ -30,8 +30,8 @@ namespace {
 // ------------------------------------------------------------------ append
 
 // Encode one new key of stream (b, h) into slot a.append_slot and copy its
-// value row: steps (1)-(4) of the pipeline for a single key, by the 128
-// threads of a query-prep workgroup.  Decisions are taken on the unnormalized
+// value row: steps (1)-(4) of the pipeline for a single key, by the threads
+// of a query-prep workgroup (at least d of them).  Decisions are taken on the unnormalized
 // transform X = sqrt(d) k~ (exact in float64 for fp16 keys): X_x^2 + X_y^2
 // against d T_j^2 and the octant comparisons of (X_x, X_y), as in the bulk
 // encoder; the residual, its norm and the QJL projection are float64.
@@ -138,13 +138,25 @@ __device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int
 
 // ------------------------------------------------------------------ query prep
 
+constexpr int kPrepThreads = 256;
+
+// One workgroup per query head: q~ = H (signs * q[perm]) / sqrt(d), the
+// per-pair angle table q~[2i] cos thetahat_a + q~[2i+1] sin thetahat_a and,
+// with QJL, S_h q~.  The kernel is latency-bound, so every global load that
+// does not depend on another is issued at the start: the thread's slice of a
+// row of S_h (kept in registers), the query row, the signs and the channel
+// order (the permuted gather then reads the query row from LDS).
 template <int D, int BM, bool QJL>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(kPrepThreads)
 query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
   constexpr int N = D / 2;
   constexpr int BA = BM - 1;
   constexpr int A = 1 << BA;
   constexpr int M = QJL ? D : 0;
+  constexpr int TPR = QJL ? kPrepThreads / (QJL ? M : 1) : 1;  // threads per row of S_h
+  constexpr int CPT = D / TPR;                                  // columns per thread
+  static_assert(!QJL || (TPR == 2 || TPR == 4), "rows of S_h per workgroup");
+  static_assert(kPrepThreads % A == 0 && kPrepThreads >= D, "thread mapping");
   const PrepLayout pl{D, N, A, M};
   const int tid = threadIdx.x;
   const int hq = blockIdx.x;
@@ -154,26 +166,41 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
   // decode step: the first query head of each kv-head appends its new token
   if (a.append_slot >= 0 && hq % a.group == 0) append_key<D, BM, QJL>(a, S, b, h, tid);
 
+  float4 srow[QJL ? CPT / 4 : 1];
+  const int r = tid / TPR, part = tid % TPR;
+  if constexpr (QJL) {
+    const float4* Sr = reinterpret_cast<const float4*>(S + (size_t(h) * M + r) * D + part * CPT);
+#pragma unroll
+    for (int k = 0; k < CPT / 4; ++k) srow[k] = Sr[k];
+  }
+  __shared__ float sraw[D];
   __shared__ float sx[D];
   __shared__ double sq64[D];
+  float sgn = 1.f;
+  int src = tid;
   if (tid < D) {
-    const int src = a.perm ? int(a.perm[size_t(h) * D + tid]) : tid;
-    float v = load_f(a.q, a.q_dtype, (size_t(b) * a.n_q + hq) * D + src);
-    if (a.hadamard) v *= float(a.signs[size_t(h) * D + tid]);
-    sx[tid] = v;
+    sraw[tid] = load_f(a.q, a.q_dtype, (size_t(b) * a.n_q + hq) * D + tid);
+    if (a.perm) src = int(a.perm[size_t(h) * D + tid]);
+    if (a.hadamard) sgn = float(a.signs[size_t(h) * D + tid]);
   }
+  // the angle grid of this thread's table entries (every entry it writes has
+  // the angle code tid % A)
+  double acs, asn;
+  sincospi(-1.0 + (2.0 * (tid % A) + 1.0) / double(A), &asn, &acs);
+  __syncthreads();
+  if (tid < D) sx[tid] = sraw[src] * sgn;
   __syncthreads();
   if (a.hadamard) {
     for (int hh = 1; hh < D; hh <<= 1) {
       float u = 0.f, w = 0.f;
       int c0 = 0;
-      if (tid < D / 2) {
+      if (tid < N) {
         c0 = (tid / hh) * 2 * hh + (tid % hh);
         u = sx[c0];
         w = sx[c0 + hh];
       }
       __syncthreads();
-      if (tid < D / 2) {
+      if (tid < N) {
         sx[c0] = u + w;
         sx[c0 + hh] = u - w;
       }
@@ -188,60 +215,115 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
     sq64[tid] = double(qt);
   }
   __syncthreads();
-  for (int e = tid; e < N * A; e += blockDim.x) {
-    const int i = e / A, ac = e % A;
-    double sn, cs;
-    sincospi(-1.0 + (2.0 * ac + 1.0) / double(A), &sn, &cs);
-    out[pl.off_lut() + e] = static_cast<float>(sq64[2 * i] * cs + sq64[2 * i + 1] * sn);
+  for (int e = tid; e < N * A; e += kPrepThreads) {
+    const int i = e / A;
+    out[pl.off_lut() + e] = static_cast<float>(sq64[2 * i] * acs + sq64[2 * i + 1] * asn);
   }
   if constexpr (QJL) {
-    // S_h q~: four adjacent threads per row of S, each reading one contiguous
-    // quarter of the row with 16-byte loads (a 128-byte line per thread at
-    // d = 128); float64 products, the quarters summed by DPP quad exchanges
-    constexpr int TPR = 4;
-    constexpr int CPT = D / TPR;
-    const int part = tid & (TPR - 1);
-    for (int r = tid / TPR; r < M; r += blockDim.x / TPR) {
-      const float4* Sr = reinterpret_cast<const float4*>(S + (size_t(h) * M + r) * D + part * CPT);
-      double acc = 0.0;
+    // S_h q~: TPR adjacent threads per row, each over a contiguous slice of
+    // CPT columns; float64 products, the slices summed by DPP quad exchanges
+    double acc = 0.0;
 #pragma unroll
-      for (int k = 0; k < CPT / 4; ++k) {
-        const float4 v = Sr[k];
-        const int c = part * CPT + 4 * k;
-        acc = fma(double(v.x), sq64[c], acc);
-        acc = fma(double(v.y), sq64[c + 1], acc);
-        acc = fma(double(v.z), sq64[c + 2], acc);
-        acc = fma(double(v.w), sq64[c + 3], acc);
-      }
-      acc += quad_xor<1>(acc);
-      acc += quad_xor<2>(acc);
-      if (part == 0) out[pl.off_sq() + r] = static_cast<float>(acc);
+    for (int k = 0; k < CPT / 4; ++k) {
+      const int c = part * CPT + 4 * k;
+      acc = fma(double(srow[k].x), sq64[c], acc);
+      acc = fma(double(srow[k].y), sq64[c + 1], acc);
+      acc = fma(double(srow[k].z), sq64[c + 2], acc);
+      acc = fma(double(srow[k].w), sq64[c + 3], acc);
     }
+    acc += quad_xor<1>(acc);
+    if constexpr (TPR == 4) acc += quad_xor<2>(acc);
+    if (part == 0) out[pl.off_sq() + r] = static_cast<float>(acc);
   }
 }
 
 // ------------------------------------------------------------------ merge
 
-__global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ partial,
-                                                    float* __restrict__ out, int d, int n_splits) {
+constexpr int kMergeThreads = 512;
+
+// Log-sum-exp merge of the split partials (m, l, o) of one query head per
+// workgroup.  The threads form J groups of d/4; a thread takes four channels
+// of the partials j, j + J, j + 2J, ... of its group, four partials at a time
+// with all their loads issued together (the kernel is latency-bound), merged
+// online (the running maximum rescales what has been summed when it grows).
+// The J group states are then combined through LDS.
+template <int D>
+__global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float* __restrict__ partial,
+                                                              float* __restrict__ out, int n_splits) {
+  constexpr int TPW = D / 4;                // threads per partial row
+  constexpr int J = kMergeThreads / TPW;    // partial groups
+  constexpr int kBlock = 4;
   const int hq = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int nq = gridDim.x;
-  const float* part = partial + (size_t(b) * nq + hq) * size_t(n_splits) * (d + 4);
   const int tid = threadIdx.x;
-  float Mx = -INFINITY;
-  for (int p = 0; p < n_splits; ++p) Mx = fmaxf(Mx, part[size_t(p) * (d + 4)]);
-  for (int dd = tid; dd < d; dd += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    if (Mx != -INFINITY) {
-      for (int p = 0; p < n_splits; ++p) {
-        const float* pp = part + size_t(p) * (d + 4);
-        const float f = exp2f(pp[0] - Mx);
-        num += f * pp[4 + dd];
-        den += f * pp[1];
+  const int q = tid % TPW, j = tid / TPW;
+  const float* part = partial + (size_t(b) * nq + hq) * size_t(n_splits) * (D + 4);
+  float Mx = -INFINITY, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = j; p0 < n_splits; p0 += J * kBlock) {
+    float mv[kBlock], lv[kBlock];
+    float4 ov[kBlock];
+#pragma unroll
+    for (int k = 0; k < kBlock; ++k) {
+      const int p = p0 + k * J;
+      const float* pp = part + size_t(p) * (D + 4);
+      const bool in = p < n_splits;
+      mv[k] = in ? pp[0] : -INFINITY;
+      lv[k] = in ? pp[1] : 0.f;
+      ov[k] = in ? *reinterpret_cast<const float4*>(pp + 4 + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float mb = Mx;
+#pragma unroll
+    for (int k = 0; k < kBlock; ++k) mb = fmaxf(mb, mv[k]);
+    if (mb != -INFINITY) {
+      const float f0 = exp2f(Mx - mb);  // 0 while nothing has been summed
+      num.x *= f0;
+      num.y *= f0;
+      num.z *= f0;
+      num.w *= f0;
+      den *= f0;
+#pragma unroll
+      for (int k = 0; k < kBlock; ++k) {
+        const float f = exp2f(mv[k] - mb);
+        num.x += f * ov[k].x;
+        num.y += f * ov[k].y;
+        num.z += f * ov[k].z;
+        num.w += f * ov[k].w;
+        den += f * lv[k];
+      }
+      Mx = mb;
+    }
+  }
+  __shared__ float s_m[J], s_l[J];
+  __shared__ float4 s_o[J][TPW];
+  s_o[j][q] = num;
+  if (q == 0) {
+    s_m[j] = Mx;
+    s_l[j] = den;
+  }
+  __syncthreads();
+  if (j == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < J; ++k) Mt = fmaxf(Mt, s_m[k]);
+    float4 nt = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dt = 0.f;
+    if (Mt != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < J; ++k) {
+        const float f = exp2f(s_m[k] - Mt);
+        const float4 o = s_o[k][q];
+        nt.x += f * o.x;
+        nt.y += f * o.y;
+        nt.z += f * o.z;
+        nt.w += f * o.w;
+        dt += f * s_l[k];
       }
     }
-    out[(size_t(b) * nq + hq) * d + dd] = den > 0.f ? num / den : 0.f;
+    const float inv = dt > 0.f ? 1.f / dt : 0.f;
+    *reinterpret_cast<float4*>(out + (size_t(b) * nq + hq) * D + 4 * q) =
+        make_float4(nt.x * inv, nt.y * inv, nt.z * inv, nt.w * inv);
   }
 }
 
@@ -250,7 +332,7 @@ __global__ void __launch_bounds__(128) merge_kernel(const float* __restrict__ pa
 template <int D, int BM, bool QJL>
 hipError_t prep_t(const DecodeArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((query_prep_kernel<D, BM, QJL>), dim3(unsigned(a.n_q), unsigned(a.n_seq)),
-                     dim3(128), 0, s, a, a.S);
+                     dim3(kPrepThreads), 0, s, a, a.S);
   return hipGetLastError();
 }
 
@@ -321,8 +403,14 @@ hipError_t launch_decode_scan(const Geometry& g, const DecodeArgs& a, bool logit
 
 hipError_t launch_partial_merge(int d, int64_t n_seq, int64_t n_q, int n_splits,
                                 const float* partial, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(n_q), unsigned(n_seq)), dim3(128), 0, s, partial,
-                     out, d, n_splits);
+  const dim3 grid(static_cast<unsigned>(n_q), static_cast<unsigned>(n_seq));
+  if (d == 64) {
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, s, partial, out, n_splits);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, s, partial, out, n_splits);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -164,12 +164,8 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
     sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], prow);
   }
   const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
-  if constexpr (WAVE_PARTS) {
-    sm.finish_wave(a.partial, row0, split * kWaves + wave, a.n_splits * kWaves);
-  } else {
-    __syncthreads();
-    sm.finish(s_merge, tid, a.n_splits, split, a.out, a.partial, row0);
-  }
+  __syncthreads();
+  sm.finish(s_merge, tid, a.n_splits, split, a.out, a.partial, row0);
 }
 
 template <int D, int G>

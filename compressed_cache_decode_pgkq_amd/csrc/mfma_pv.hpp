@@ -161,23 +161,10 @@ struct MfmaPV {
   // Lane l holds, for head g = 4(l/16) + r, channels 16n + l%16 of o in acc[n][r].
   __device__ __forceinline__ bool owns(int g) const { return (lane >> 4) == (g >> 2); }
 
-  __device__ __forceinline__ void finish_wave(float* __restrict__ partial, size_t row0, int pidx,
-                                              int n_parts) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float l_w = wave_sum(l_lane[g]);
-      float* part = partial + ((row0 + g) * n_parts + pidx) * (D + 4);
-      if (owns(g)) {
-#pragma unroll
-        for (int n = 0; n < NT; ++n) part[4 + 16 * n + (lane & 15)] = acc[n][g & 3];
-      }
-      if (lane == 0) {
-        part[0] = m_run[g];
-        part[1] = l_w;
-      }
-    }
-  }
-
+  // Merge the wavefronts of the workgroup through `scratch` (MERGE_FLOATS
+  // floats of LDS, free to reuse: the caller synchronizes before) and write
+  // the final output rows (n_splits == 1) or partial `split` of each query head
+  // row0 .. row0 + G - 1.
   __device__ __forceinline__ void finish(float* scratch, int tid, int n_splits, int split,
                                          float* __restrict__ out, float* __restrict__ partial,
                                          size_t row0) {

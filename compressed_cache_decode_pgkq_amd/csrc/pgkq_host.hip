@@ -73,8 +73,8 @@ bool fits_buffer(int64_t capacity, size_t record_bytes, int d) {
 struct Splits {
   int n;             // workgroups per (sequence, kv-head)
   int64_t tokens_per;  // tokens per workgroup
-  int wave_parts;    // 1: one partition per wavefront (4 per workgroup)
-  int partials() const { return wave_parts ? 4 * n : n; }
+  int wave_parts;    // 1: one partition per wavefront (merged in the workgroup)
+  int partials() const { return n; }
 };
 
 constexpr int kScanWaves = 4;

@@ -261,12 +261,8 @@ rtn_scan_kernel(RtnDecodeArgs a, const uint8_t* __restrict__ codes, const __half
   }
   if constexpr (!LOGITS) {
     const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
-    if (a.wave_parts) {
-      sm.finish_wave(a.partial, row0, split * kWaves + wave, a.n_splits * kWaves);
-    } else {
-      __syncthreads();
-      sm.finish(s_merge, tid, a.n_splits, split, a.out, a.partial, row0);
-    }
+    __syncthreads();
+    sm.finish(s_merge, tid, a.n_splits, split, a.out, a.partial, row0);
   }
 }
 

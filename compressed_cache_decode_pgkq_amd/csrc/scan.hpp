@@ -274,20 +274,12 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   if constexpr (CODED_V && !LOGITS) {
     // partial states only (the merge kernel applies S_v^T)
     const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
-    if (a.wave_parts) {
-      sm.finish_wave(a.partial, row0, split * kScanWaves + wave, a.n_splits * kScanWaves);
-    } else {
-      __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
-      sm.finish(s_tab, tid, a.partial, row0, split, a.n_splits);
-    }
+    __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
+    sm.finish(s_tab, tid, a.partial, row0, split, a.n_splits);
   } else if constexpr (!LOGITS) {
     const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;
-    if (a.wave_parts) {
-      sm.finish_wave(a.partial, row0, split * kScanWaves + wave, a.n_splits * kScanWaves);
-    } else {
-      __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
-      sm.finish(s_tab, tid, a.n_splits, split, a.out, a.partial, row0);
-    }
+    __syncthreads();  // tables are dead; their LDS holds the cross-wave merge
+    sm.finish(s_tab, tid, a.n_splits, split, a.out, a.partial, row0);
   }
 }
 
