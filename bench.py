@@ -192,6 +192,56 @@ def run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E, reps: in
     return res
 
 
+def run_other_workloads(api, torch, dev, flush, E, reps: int = 20):
+    """Decode of the other configurations of the pages' workload list on this
+    GPU (NanoGPT-256 context with and without QJL, the 131k-token single
+    stream): whole decode call and scan kernel, keys encoded and values packed
+    beforehand (inputs resident)."""
+    from synth import CONFIGS, make_inputs
+    res = {}
+    for name in ("nano_b64_t512", "nano_b64_t512_b4", "gqa_b1_t131k"):
+        cfg = CONFIGS[name]
+        inp = make_inputs(cfg)
+        n_seq, n_kv, T, d = inp["K"].shape
+        p = api.PgkqParams(d, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
+        K = torch.from_numpy(inp["K"]).to(dev)
+        Vt = api.pgkq_pack_values(torch.from_numpy(inp["V"]).to(dev))
+        q = torch.from_numpy(inp["q"]).to(dev)
+        if cfg.q_dtype == "bf16":
+            q = q.to(torch.bfloat16)
+        signs = torch.from_numpy(inp["signs"]).to(dev)
+        S = torch.from_numpy(inp["S"]).to(dev) if cfg.qjl_m else None
+        _, perm, cb = api.pgkq_calibrate(p, K)
+        codes = api.pgkq_encode(p, K, signs, None, cb, S, capacity=T)
+        out = torch.empty((n_seq, cfg.n_q, d), dtype=torch.float32, device=dev)
+        ws = torch.empty(api.pgkq_decode_workspace_bytes(p, n_seq, cfg.n_q, n_kv, T, cfg.n_splits),
+                         dtype=torch.uint8, device=dev)
+        e0, e1, c0, c1 = E(), E(), E(), E()
+        e0.record()
+        e1.record()
+        scan, call = [], []
+        for r in range(reps + 3):
+            flush.fill_(r & 255)
+            c0.record()
+            api.pgkq_decode_attn(p, q, codes, Vt, signs, None, cb, S, n_splits=cfg.n_splits, out=out,
+                                 workspace=ws, events=(e0, e1))
+            c1.record()
+            torch.cuda.synchronize()
+            if r >= 3:
+                scan.append(e0.elapsed_time(e1))
+                call.append(c0.elapsed_time(c1))
+        scan_ms, call_ms = float(np.median(scan)), float(np.median(call))
+        rb = api.pgkq_record_bytes(p)
+        alg = n_seq * n_kv * T * (rb + 2 * d)
+        res[name] = {"description": cfg.description, "record_bytes": rb,
+                     "decode_call_ms": call_ms, "scan_ms": scan_ms,
+                     "cache_tokens_per_s": n_seq * T / (call_ms * 1e-3),
+                     "scan_gbs": alg / (scan_ms * 1e-3) / 1e9,
+                     "scan_frac": alg / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del K, Vt, q, codes, ws, inp
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +334,7 @@ def main():
                      "p90": float(np.percentile(ph[:, k], 90))}
     copy_gbs = measure_copy(torch, dev)
     controls = run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E)
+    others = run_other_workloads(api, torch, dev, flush, E)
 
     token_heads = n_seq * n_kv * T
     alg_bytes = token_heads * (rb + 2 * d)
@@ -341,6 +392,7 @@ def main():
                      "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean,
                      "measured_copy_gbs": copy_gbs},
         "controls": controls,
+        "other_workloads": others,
     }
     if not args.no_cpu_baseline:
         cb_res = cpu_baseline(cfg, inp)
