@@ -49,6 +49,13 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _half(t):
+    """Device pointer of an fp16 tensor (value caches, value rows, fp16 keys)."""
+    if t is not None and t.dtype != torch.float16:
+        raise TypeError(f"expected a float16 tensor, got {t.dtype}")
+    return _ptr(t)
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -159,7 +166,7 @@ def pgkq_decode_attn(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, V
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_decode_attn(ctypes.byref(p), _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap,
                                   _ptr(signs), _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes),
-                                  _ptr(V), _ptr(out), float(softmax_scale), ctypes.byref(o),
+                                  _half(V), _ptr(out), float(softmax_scale), ctypes.byref(o),
                                   _ptr(ws), wsb, _stream(stream))
     L.check(st, "pgkq_decode_attn")
     return out
@@ -181,8 +188,8 @@ def pgkq_decode_step(params: PgkqParams, q: torch.Tensor, k_new: torch.Tensor,
                                                   int(n_cached) + 1, ctypes.byref(o)))
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_decode_step(ctypes.byref(p), _ptr(q), _dtype(q), _ptr(k_new), _dtype(k_new),
-                                  _ptr(v_new), n_seq, n_q, n_kv, int(n_cached), cap, _ptr(signs),
-                                  _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes), _ptr(V),
+                                  _half(v_new), n_seq, n_q, n_kv, int(n_cached), cap, _ptr(signs),
+                                  _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes), _half(V),
                                   _ptr(out), float(softmax_scale), ctypes.byref(o), _ptr(ws), wsb,
                                   _stream(stream))
     L.check(st, "pgkq_decode_step")
@@ -233,7 +240,7 @@ def pgkq_pack_values(rows: torch.Tensor, capacity=None, cache=None, slot_offset:
         cache = torch.zeros((n_seq, n_kv, cap, d), dtype=torch.float16, device=rows.device)
     cap = cache.shape[2]
     rows = rows.contiguous()
-    st = L.lib().pgkq_pack_values(_ptr(rows), n_seq * n_kv, T, d, _ptr(cache), cap, int(slot_offset),
+    st = L.lib().pgkq_pack_values(_half(rows), n_seq * n_kv, T, d, _half(cache), cap, int(slot_offset),
                                   _stream(stream))
     L.check(st, "pgkq_pack_values")
     return cache
@@ -245,7 +252,7 @@ def pgkq_unpack_values(cache: torch.Tensor, n_tokens=None, slot_offset: int = 0,
     n_seq, n_kv, cap, d = cache.shape
     T = cap - int(slot_offset) if n_tokens is None else int(n_tokens)
     rows = torch.empty((n_seq, n_kv, T, d), dtype=torch.float16, device=cache.device)
-    st = L.lib().pgkq_unpack_values(_ptr(cache), n_seq * n_kv, cap, d, int(slot_offset), T,
+    st = L.lib().pgkq_unpack_values(_half(cache), n_seq * n_kv, cap, d, int(slot_offset), T,
                                     _ptr(rows), _stream(stream))
     L.check(st, "pgkq_unpack_values")
     return rows
@@ -264,7 +271,7 @@ def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor,
     nb = int(L.lib().pgkq_fp16_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, ctypes.byref(o)))
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_fp16_decode_attn(_ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap, d,
-                                       _ptr(K16), _ptr(V16), _ptr(out), float(softmax_scale),
+                                       _half(K16), _half(V16), _ptr(out), float(softmax_scale),
                                        ctypes.byref(o), _ptr(ws) if ws is not None else None, wsb,
                                        _stream(stream))
     L.check(st, "pgkq_fp16_decode_attn")
@@ -345,7 +352,7 @@ def pgkq_rtn_decode_attn(q: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, 
     nb = int(L.lib().pgkq_rtn_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, ctypes.byref(o)))
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_rtn_decode_attn(d, bits, _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap,
-                                      _ptr(codes), _ptr(V), _ptr(out), float(softmax_scale),
+                                      _ptr(codes), _half(V), _ptr(out), float(softmax_scale),
                                       ctypes.byref(o), _ptr(ws), wsb, _stream(stream))
     L.check(st, "pgkq_rtn_decode_attn")
     return out
