@@ -80,10 +80,10 @@ struct DecodeArgs {
   float* out;           // final output (n_splits == 1) or null
   float* logits;        // logits mode output or null
   float* prep;          // workspace: query prep
-  float* partial;       // workspace: partial states [n_seq][n_q][n_partials][d + 4]
+  float* partial;       // workspace: partial states [n_seq][n_q][n_splits][d + 4]
   int n_splits;         // workgroups per (sequence, kv-head)
   int64_t tokens_per_split;
-  int wave_parts;       // 1: each wavefront scans its own partition (n_partials = 4 n_splits)
+  int wave_parts;       // 1: each wavefront scans a contiguous partition of the split
   float scale_log2;     // softmax scale * log2(e)
   // decode step: before the scan, the query-prep launch encodes k_new (one key
   // per stream) into slot append_slot of `codes_w` and copies v_new into the
@@ -114,7 +114,7 @@ struct Fp16DecodeArgs {
   float* partial;
   int n_splits;
   int64_t tokens_per_split;
-  int wave_parts;       // 1: each wavefront scans its own partition
+  int wave_parts;       // 1: each wavefront scans a contiguous partition of the split
   float scale_log2;
 };
 

@@ -187,7 +187,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
 
   // Token ranges: either the workgroup's split is shared by its wavefronts in
   // interleaved chunks, or (wave_parts) every wavefront scans a contiguous
-  // partition of its own and writes its own partial state.
+  // partition of it; either way the wavefronts are merged in the workgroup.
   int64_t c_first, c_end, c_step;
   if (a.wave_parts) {
     const int64_t tpw = a.tokens_per_split / kScanWaves;
