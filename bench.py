@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -42,12 +43,36 @@ SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/scan.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
 
 
-def scan_source_hash() -> str:
+ENCODE_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/encode.hip",
+                  "compressed_cache_decode_pgkq_amd/csrc/pgkq_internal.hpp",
+                  "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
+PROFILE_UTIL = os.path.join(ROOT, "profiles", "utilization_gqa32k_b16.json")
+ENCODE_KERNEL = "void encode_kernel<128, 3, true, 2>"
+# vector ALU issue rate: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz (a
+# wave64 instruction occupies its SIMD for 4 clocks); an fp64 FMA is one
+# lane-operation, so this is also the published fp64 vector peak / 2
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def _source_hash(files) -> str:
+    """Hash of the code of `files` (comments and blank space removed, so that a
+    profile stays attached to kernels whose code has not changed)."""
     h = hashlib.sha256()
-    for rel in SCAN_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in files:
+        with open(os.path.join(ROOT, rel)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
+
+
+def scan_source_hash() -> str:
+    return _source_hash(SCAN_SOURCES)
+
+
+def encode_source_hash() -> str:
+    return _source_hash(ENCODE_SOURCES)
 
 
 def log(*a):
@@ -364,6 +389,15 @@ def main():
         if tr.get("source_hash") == scan_source_hash():
             traffic = tr.get("bytes_per_launch")
     n_keys = n_seq * n_kv * T
+    # the encoder's binding resource is the vector ALU: issued lane-operations
+    # per key from the committed instruction-count profile of the same sources
+    enc_valu = None
+    if os.path.exists(PROFILE_UTIL):
+        with open(PROFILE_UTIL) as f:
+            ut = json.load(f)
+        kern = ut.get("kernels", {}).get(ENCODE_KERNEL)
+        if ut.get("encode_source_hash") == encode_source_hash() and kern:
+            enc_valu = kern["valu_instr_per_unit"] * 64.0
     enc_flops = n_keys * 2.0 * cfg.qjl_m * d
     enc_gbs = n_keys * (2 * d + rb) / (enc_ms * 1e-3) / 1e9
     result = {
@@ -398,11 +432,20 @@ def main():
                    "keys_per_s_with_calibrate": n_keys / ((enc_ms + cal_ms) * 1e-3),
                    "hbm_gbs": enc_gbs,
                    "projection_tflops": enc_flops / (enc_ms * 1e-3) / 1e12,
-                   # keys in, records out; the kernel is bound by its float64 vector
-                   # work (transform and decisions), not by HBM or the MFMA projection
-                   "roofline": {"bound": "hbm", "achieved": enc_gbs, "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s", "frac": enc_gbs / HBM_PEAK_GBS, "traffic": None,
-                                "note": "VALU-bound (float64 transform and code decisions)"}},
+                   # bound by its float64 vector work (transform and decisions):
+                   # issued VALU lane-operations per second against the issue rate;
+                   # HBM and the split-fp16 MFMA projection are far from their peaks
+                   "roofline": {"bound": "alu",
+                                "achieved": (enc_valu * n_keys / (enc_ms * 1e-3) / 1e12) if enc_valu else None,
+                                "peak": VALU_PEAK_LANE_OPS / 1e12, "unit": "T lane-op/s",
+                                "frac": (enc_valu * n_keys / (enc_ms * 1e-3) / VALU_PEAK_LANE_OPS) if enc_valu else None,
+                                "lane_ops_per_key": enc_valu,
+                                "hbm_frac": enc_gbs / HBM_PEAK_GBS,
+                                "mfma_frac": enc_flops * 3 / (enc_ms * 1e-3) / 2.5e15,
+                                "note": "lane-ops per key from the profiled VALU instruction count "
+                                        "(profiles/utilization_gqa32k_b16.json); mfma_frac counts the "
+                                        "three split-fp16 products per projection flop against the "
+                                        "2.5 PFLOP/s fp16 peak"}},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean,
