@@ -50,7 +50,10 @@ struct EncodeSmem {
 // x ~ hi + lo with fp16 parts: the fp32 rounding of x costs 2^-24 relative,
 // the fp16 remainder about 2^-22; hi - xf is exact in fp32
 __device__ __forceinline__ void split_f16(double x, _Float16& hi, _Float16& lo) {
-  const float xf = static_cast<float>(x);
+  float xf = static_cast<float>(x);
+  // keep the fp32 value: otherwise the two narrowings fold into one float64 ->
+  // fp16 conversion, which the hardware lacks and which costs ~30 instructions
+  pin_reg(xf);
   hi = static_cast<_Float16>(xf);
   lo = static_cast<_Float16>(xf - static_cast<float>(hi));
 }
