@@ -39,22 +39,36 @@ __global__ void __launch_bounds__(kThreads) calib_partial_kernel(CalibArgs a) {
   double acc[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) acc[e] = 0.0;
-  for (int64_t t = t0 + rp; t < t1; t += RPP) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(base + t * int64_t(D) * ESIZE);
+  auto row = [&](int64_t t) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + t * int64_t(D) * ESIZE));
+  };
+  auto add = [&](const u32x4& raw) {
     if constexpr (ESIZE == 2) {
-      const __half2* hv = reinterpret_cast<const __half2*>(&raw);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float2 f = __half22float2(hv[k]);
-        acc[2 * k] += double(f.x) * double(f.x);
-        acc[2 * k + 1] += double(f.y) * double(f.y);
+        const float fx = __half2float(__ushort_as_half(static_cast<uint16_t>(raw[k])));
+        const float fy = __half2float(__ushort_as_half(static_cast<uint16_t>(raw[k] >> 16)));
+        acc[2 * k] += double(fx) * double(fx);
+        acc[2 * k + 1] += double(fy) * double(fy);
       }
     } else {
-      const float* fv = reinterpret_cast<const float*>(&raw);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += double(fv[k]) * double(fv[k]);
+      for (int k = 0; k < 4; ++k) {
+        const float f = __uint_as_float(raw[k]);
+        acc[k] += double(f) * double(f);
+      }
     }
+  };
+  // four rows in flight per thread; the sums still run over the rows in order
+  int64_t t = t0 + rp;
+  for (; t + 3 * RPP < t1; t += 4 * RPP) {
+    const u32x4 r0 = row(t), r1 = row(t + RPP), r2 = row(t + 2 * RPP), r3 = row(t + 3 * RPP);
+    add(r0);
+    add(r1);
+    add(r2);
+    add(r3);
   }
+  for (; t < t1; t += RPP) add(row(t));
   __shared__ double s_acc[RPP][D];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) s_acc[rp][cg * EPT + e] = acc[e];
