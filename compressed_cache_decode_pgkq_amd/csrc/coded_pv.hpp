@@ -13,8 +13,8 @@
 //     the partial states, is left to the merge kernel (one matrix-vector
 //     product per query head instead of one per partition).
 // The chunk's code words arrive lane = token (coalesced dword loads) and are
-// transposed through a wave-private LDS block.  Every wavefront writes its own
-// partial state (m, l, o[d], a[m]).
+// transposed through a wave-private LDS block.  The wavefronts' states
+// (m, l, o[d], a[m]) are merged in the workgroup into one partial per split.
 #pragma once
 
 #include "device_common.hpp"
