@@ -339,6 +339,19 @@ hipError_t prep_t(const DecodeArgs& a, hipStream_t s) {
 template <int D, int BM, bool QJL, int G>
 hipError_t scan_t(const DecodeArgs& a, bool logits_mode, hipStream_t s) {
   dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
+  if constexpr (G <= kFusedPrepMaxGroup) {
+    if (a.fused_prep) {
+      if (logits_mode) {
+        hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, true, 0, true>), grid, dim3(kScanThreads),
+                           0, s, a, a.codes, a.V);
+      } else {
+        hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, false, 0, true>), grid,
+                           dim3(kScanThreads), 0, s, a, a.codes, a.V);
+      }
+      return hipGetLastError();
+    }
+  }
+  if (a.fused_prep) return hipErrorInvalidValue;
   if (logits_mode) {
     hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, true>), grid, dim3(kScanThreads), 0, s, a,
                        a.codes, a.V);

@@ -531,6 +531,10 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   a.n_splits = sp.n;
   a.tokens_per_split = sp.tokens_per;
   a.wave_parts = sp.wave_parts;
+  // one workgroup per stream: the scan prepares the query itself (no extra
+  // launch, nothing repeated); a decode step keeps the separate launch, which
+  // also appends the new token
+  a.fused_prep = (sp.n == 1 && !sp.wave_parts && !step && group <= pgkq::kFusedPrepMaxGroup) ? 1 : 0;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(g.d));
   a.scale_log2 = scale * 1.4426950408889634f;
   a.append_slot = -1;
@@ -542,8 +546,11 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
     a.codes_w = static_cast<uint8_t*>(const_cast<void*>(codes));
     a.V_w = static_cast<__half*>(const_cast<void*>(V));
   }
-  hipError_t e = pgkq::launch_query_prep(g, a, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  hipError_t e = hipSuccess;
+  if (!a.fused_prep) {
+    e = pgkq::launch_query_prep(g, a, s);
+    if (e != hipSuccess) return PGKQ_ERR_HIP;
+  }
   if (opts && opts->scan_start) {
     if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
       return PGKQ_ERR_HIP;

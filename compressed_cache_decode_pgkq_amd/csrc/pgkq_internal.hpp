@@ -84,6 +84,7 @@ struct DecodeArgs {
   int n_splits;         // workgroups per (sequence, kv-head)
   int64_t tokens_per_split;
   int wave_parts;       // 1: each wavefront scans a contiguous partition of the split
+  int fused_prep;       // 1: the scan prepares the query itself (one workgroup per stream)
   float scale_log2;     // softmax scale * log2(e)
   // decode step: before the scan, the query-prep launch encodes k_new (one key
   // per stream) into slot append_slot of `codes_w` and copies v_new into the
@@ -166,6 +167,9 @@ struct ValuesArgs {
 hipError_t launch_values(const ValuesArgs& a, hipStream_t s);
 hipError_t launch_calibrate(const CalibArgs& a, hipStream_t s);
 hipError_t launch_encode(const Geometry& g, const EncodeArgs& a, hipStream_t s);
+// largest query-head group for which the scan can prepare the query itself
+constexpr int kFusedPrepMaxGroup = 2;
+
 hipError_t launch_query_prep(const Geometry& g, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_scan(const Geometry& g, const DecodeArgs& a, bool logits_mode,
                               hipStream_t s);

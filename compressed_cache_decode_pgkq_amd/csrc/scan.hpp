@@ -62,7 +62,130 @@ template <int D, int G, int VB, bool QJL>
 using ValuePath = std::conditional_t<(VB > 0), CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>,
                                      MfmaPV<D, G, kScanWaves>>;
 
-template <int D, int BM, bool QJL, int G, bool LOGITS, int VB = 0>
+// Query preparation inside the scan (FUSED): used when every (sequence,
+// kv-head) stream is one workgroup, so that no preparation is repeated; the
+// results are bit-identical to the separate preparation kernel (same
+// operations in the same order).
+template <int D, int BM, bool QJL, int G>
+struct FusedPrep {
+  static constexpr int N = D / 2;
+  static constexpr int A = 1 << (BM - 1);
+  static constexpr int M = QJL ? D : 0;
+  static constexpr int TPR = QJL ? kScanThreads / (QJL ? M : 1) : 1;  // threads per row of S_h
+  static constexpr int CPT = D / TPR;                                  // columns per thread
+  static_assert(!QJL || TPR == 2 || TPR == 4, "rows of S_h per workgroup");
+
+  double q64[G][D];  // q~ as float64 (the raw query rows before)
+  float qf[G][D];    // the gathered rows, transformed in place
+  float sq[QJL ? G : 1][QJL ? M : 1];
+  double2 grid[A];   // (cos, sin) of the angle grid
+
+  __device__ __forceinline__ void run(const DecodeArgs& a, int64_t b, int h, int tid) {
+    constexpr int QE = (G * D + kScanThreads - 1) / kScanThreads;
+    float4 srow[QJL ? CPT / 4 : 1];
+    if constexpr (QJL) {  // the thread's slice of a row of S_h, first
+      const float4* Sr = reinterpret_cast<const float4*>(a.S + (size_t(h) * M + tid / TPR) * D +
+                                                         (tid % TPR) * CPT);
+#pragma unroll
+      for (int k = 0; k < CPT / 4; ++k) srow[k] = Sr[k];
+    }
+    {
+      float* qraw = reinterpret_cast<float*>(&q64[0][0]);
+      int src[QE];
+      float sgn[QE];
+#pragma unroll
+      for (int k = 0; k < QE; ++k) {
+        const int e = tid + k * kScanThreads;
+        src[k] = 0;
+        sgn[k] = 1.f;
+        if (e < G * D) {
+          const int g = e / D, c = e % D;
+          qraw[e] = load_f(a.q, a.q_dtype, (size_t(b) * a.n_q + size_t(h) * G + g) * D + c);
+          src[k] = g * D + (a.perm ? int(a.perm[size_t(h) * D + c]) : c);
+          if (a.hadamard) sgn[k] = float(a.signs[size_t(h) * D + c]);
+        }
+      }
+      if (tid < A) {
+        double sn, cs;
+        sincospi(-1.0 + (2.0 * tid + 1.0) / double(A), &sn, &cs);
+        grid[tid] = make_double2(cs, sn);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < QE; ++k) {
+        const int e = tid + k * kScanThreads;
+        if (e < G * D) (&qf[0][0])[e] = qraw[src[k]] * sgn[k];
+      }
+      __syncthreads();
+    }
+    if (a.hadamard) {
+      constexpr int BE = (G * N + kScanThreads - 1) / kScanThreads;
+      for (int hh = 1; hh < D; hh <<= 1) {
+        float u[BE], w[BE];
+        int at[BE];
+#pragma unroll
+        for (int k = 0; k < BE; ++k) {
+          const int e = tid + k * kScanThreads;
+          at[k] = -1;
+          if (e < G * N) {
+            const int g = e / N, j = e % N;
+            at[k] = g * D + (j / hh) * 2 * hh + (j % hh);
+            u[k] = (&qf[0][0])[at[k]];
+            w[k] = (&qf[0][0])[at[k] + hh];
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < BE; ++k) {
+          if (at[k] >= 0) {
+            (&qf[0][0])[at[k]] = u[k] + w[k];
+            (&qf[0][0])[at[k] + hh] = u[k] - w[k];
+          }
+        }
+        __syncthreads();
+      }
+    }
+    const float sc = a.hadamard ? 1.0f / sqrtf(float(D)) : 1.0f;
+#pragma unroll
+    for (int k = 0; k < QE; ++k) {
+      const int e = tid + k * kScanThreads;
+      if (e < G * D) (&q64[0][0])[e] = double((&qf[0][0])[e] * sc);
+    }
+    __syncthreads();
+    if constexpr (QJL) {
+      // S_h q~: float64 products over the thread's slice in column order, the
+      // slices summed by DPP quad exchanges
+      const int c0 = (tid % TPR) * CPT;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        double acc = 0.0;
+#pragma unroll
+        for (int k = 0; k < CPT / 4; ++k) {
+          float4 v = srow[k];
+          pin_reg(v.x);  // converted where used, not all CPT doubles at once
+          pin_reg(v.y);
+          pin_reg(v.z);
+          pin_reg(v.w);
+          acc = fma(double(v.x), q64[g][c0 + 4 * k], acc);
+          acc = fma(double(v.y), q64[g][c0 + 4 * k + 1], acc);
+          acc = fma(double(v.z), q64[g][c0 + 4 * k + 2], acc);
+          acc = fma(double(v.w), q64[g][c0 + 4 * k + 3], acc);
+        }
+        acc += quad_xor<1>(acc);
+        if constexpr (TPR == 4) acc += quad_xor<2>(acc);
+        if (tid % TPR == 0) sq[g][tid / TPR] = static_cast<float>(acc);
+      }
+    }
+    __syncthreads();
+  }
+
+  // angle table entry of pair i, angle code ac, head g
+  __device__ __forceinline__ float lut(int g, int i, int ac) const {
+    return static_cast<float>(q64[g][2 * i] * grid[ac].x + q64[g][2 * i + 1] * grid[ac].y);
+  }
+};
+
+template <int D, int BM, bool QJL, int G, bool LOGITS, int VB = 0, bool FUSED = false>
 __global__ void __launch_bounds__(kScanThreads, kScanMinWavesPerEU)
 decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half* __restrict__ V) {
   using VP = ValuePath<D, G, VB, QJL>;
@@ -87,6 +210,9 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   constexpr int VTAB = CODED_V ? (1 << (2 * VB - 1)) : 1;
   __shared__ __align__(16) uint32_t s_vw[kScanWaves][VW_WORDS];
   __shared__ __align__(16) float2 s_vtab[VTAB];
+  using FP = FusedPrep<D, BM, QJL, (FUSED ? G : 1)>;
+  __shared__ __align__(16) unsigned char s_fused_raw[FUSED ? sizeof(FP) : 16];
+  FP& fp = *reinterpret_cast<FP*>(s_fused_raw);
 
   const int tid = threadIdx.x;
   const int split = blockIdx.x;
@@ -134,6 +260,8 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     if constexpr (QJL) nu = half_bits_to_float(buf_load_b16(crs, nu_off + t4 / 2));
   };
 
+  if constexpr (FUSED) fp.run(a, b, h, tid);
+
   // ---- tables: one thread per (pair, query head)
   {
     float lvr[L];
@@ -141,10 +269,15 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     for (int r = 0; r < L; ++r) lvr[r] = lv[r];
     for (int ig = tid; ig < N * G; ig += kScanThreads) {
       const int i = ig / G, g = ig % G;
-      const float* lut = prep0 + size_t(g) * pl.stride() + pl.off_lut() + i * A;
       float lt[A];
+      if constexpr (FUSED) {
 #pragma unroll
-      for (int ac = 0; ac < A; ++ac) lt[ac] = lut[ac];
+        for (int ac = 0; ac < A; ++ac) lt[ac] = fp.lut(g < (FUSED ? G : 1) ? g : 0, i, ac);
+      } else {
+        const float* lut = prep0 + size_t(g) * pl.stride() + pl.off_lut() + i * A;
+#pragma unroll
+        for (int ac = 0; ac < A; ++ac) lt[ac] = lut[ac];
+      }
       if constexpr (JOINT) {
 #pragma unroll
         for (int code = 0; code < NCODES; ++code)
@@ -173,7 +306,8 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     const float kappa = 1.2533141373155003f / float(M);  // sqrt(pi/2) / m
     for (int kg = tid; kg < (M / 4) * G; kg += kScanThreads) {
       const int k = kg / G, g = kg % G;
-      const float* sq = prep0 + size_t(g) * pl.stride() + pl.off_sq() + 4 * k;
+      const float* sq = FUSED ? &fp.sq[g < (FUSED ? G : 1) ? g : 0][QJL && FUSED ? 4 * k : 0]
+                              : prep0 + size_t(g) * pl.stride() + pl.off_sq() + 4 * k;
       const float q0 = sq[0], q1 = sq[1], q2 = sq[2], q3 = sq[3];
 #pragma unroll
       for (int nib = 0; nib < 16; ++nib) {
