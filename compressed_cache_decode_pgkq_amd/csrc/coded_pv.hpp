@@ -3,11 +3,11 @@
 // page, PGKQ-KV paragraphs).
 //
 // The output sum_t p_t V-hat_t is accumulated in the code domain:
-//   * pair part: lane = 8 channels (4 pairs) of a token row, as for fp16
-//     values; each pair's joint code indexes a 2^P-entry LDS table of
+//   * pair part: lane = CPL channels (CPL / 2 pairs) of a token row; each
+//     pair's joint code indexes a 2^P-entry LDS table of
 //     (level[rc] cos thetahat[ac], level[rc] sin thetahat[ac]) and is weighted
 //     by p_t;
-//   * QJL part: the same lane owns 8 sketch bits; it accumulates
+//   * QJL part: the same lane owns CPL sketch bits; it accumulates
 //     sum_t p_t nu_t bit_tj and sum_t p_t nu_t, giving
 //     a_j = sum_t p_t nu_t (2 bit_tj - 1).  The product kappa S^T a, linear in
 //     the partial states, is left to the merge kernel (one matrix-vector
@@ -15,6 +15,8 @@
 // The chunk's code words arrive lane = token (coalesced dword loads) and are
 // transposed through a wave-private LDS block.  The wavefronts' states
 // (m, l, o[d], a[m]) are merged in the workgroup into one partial per split.
+// A lane holds 2 G CPL accumulators: CPL = 8 up to 4 query heads, 4 for 8 heads
+// (twice the rows per lane, half the registers).
 #pragma once
 
 #include "device_common.hpp"
@@ -30,7 +32,9 @@ struct CodedPV {
   static constexpr int NC = N * P / 32;        // code words per token
   static constexpr int NW = NC + M / 32;       // words per token
   static constexpr int NROW = NW + (QJLV ? 1 : 0);  // LDS rows per chunk: words, norms
-  static constexpr int LPT = D / 8;            // lanes per token row
+  static constexpr int CPL = G >= 8 ? 4 : 8;    // channels per lane
+  static constexpr int PPL = CPL / 2;           // pairs per lane
+  static constexpr int LPT = D / CPL;           // lanes per token row
   static constexpr int TPI = kWave / LPT;      // rows per pass
   static constexpr int NIT = kWave / TPI;      // passes per chunk
   static constexpr int WIDTH = 2 * D + 4;      // partial row: m, l, -, -, o[D], a[D]
@@ -39,9 +43,10 @@ struct CodedPV {
   // one LDS bank
   static constexpr int VW_STRIDE = kWave + 1;
   static constexpr int LDS_WORDS = NROW * VW_STRIDE;
-  static_assert(4 * P <= 32, "a lane's four pair codes span at most two words");
+  static_assert(PPL * P <= 32, "a lane's pair codes span at most two words");
+  static_assert(LPT <= kWave, "lanes per token row");
 
-  float m_run[G], l_lane[G], o[G][8], acc[G][8], spn[G];
+  float m_run[G], l_lane[G], o[G][CPL], acc[G][CPL], spn[G];
   int lane, wave, slot, dblk;
   uint32_t row_bytes, nu_off;
 
@@ -63,7 +68,7 @@ struct CodedPV {
       l_lane[g] = 0.f;
       spn[g] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < CPL; ++k) {
         o[g][k] = 0.f;
         acc[g][k] = 0.f;
       }
@@ -95,7 +100,7 @@ struct CodedPV {
         l_lane[g] *= alpha;
         spn[g] *= alpha;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < CPL; ++k) {
           o[g][k] *= alpha;
           acc[g][k] *= alpha;
         }
@@ -118,7 +123,7 @@ struct CodedPV {
     if constexpr (QJLV) vw[NW * VW_STRIDE + lane] = vc.nu;
     wave_lds_sync();
 
-    const int o0 = 4 * P * dblk;  // first polar bit of this lane's pairs
+    const int o0 = PPL * P * dblk;  // first polar bit of this lane's pairs
     const int w0 = o0 >> 5, sh = o0 & 31;
     const int w1 = w0 + 1 < NROW ? w0 + 1 : NROW - 1;
     constexpr uint32_t mask = (1u << P) - 1u;
@@ -130,7 +135,7 @@ struct CodedPV {
       lds_fetch<G>(p_rows + r * G, pp);
       const uint64_t bits = uint64_t(vw[w0 * VW_STRIDE + r]) | (uint64_t(vw[w1 * VW_STRIDE + r]) << 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < PPL; ++j) {
         const uint32_t code = static_cast<uint32_t>(bits >> (sh + P * j)) & mask;
         const float2 t = vtab[code];
 #pragma unroll
@@ -140,18 +145,20 @@ struct CodedPV {
         }
       }
       if constexpr (QJLV) {
-        const uint32_t sb = (vw[(NC + (dblk >> 2)) * VW_STRIDE + r] >> (8 * (dblk & 3))) & 0xFFu;
+        constexpr uint32_t smask = (1u << CPL) - 1u;
+        const uint32_t sb =
+            (vw[(NC + (CPL * dblk) / 32) * VW_STRIDE + r] >> ((CPL * dblk) & 31)) & smask;
         const float nu = half_bits_to_float(static_cast<uint16_t>(vw[NW * VW_STRIDE + r]));
         const bool live = c0 + r < c_end;  // a slot past the cache may hold any bits
-        float fb[8];
+        float fb[CPL];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) fb[k] = static_cast<float>((sb >> k) & 1u);
+        for (int k = 0; k < CPL; ++k) fb[k] = static_cast<float>((sb >> k) & 1u);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const float pn = live ? pp[g] * nu : 0.f;
           spn[g] += pn;
 #pragma unroll
-          for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(fb[k], pn, acc[g][k]);
+          for (int k = 0; k < CPL; ++k) acc[g][k] = fmaf(fb[k], pn, acc[g][k]);
         }
       }
     }
@@ -166,7 +173,7 @@ struct CodedPV {
       for (int g = 0; g < G; ++g) {
         spn[g] += __shfl_xor(spn[g], off, kWave);
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < CPL; ++k) {
           o[g][k] += __shfl_xor(o[g][k], off, kWave);
           acc[g][k] += __shfl_xor(acc[g][k], off, kWave);
         }
@@ -192,9 +199,9 @@ struct CodedPV {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          wo[(wave * G + g) * 2 * D + dblk * 8 + k] = o[g][k];
-          wo[(wave * G + g) * 2 * D + D + dblk * 8 + k] = QJLV ? 2.f * acc[g][k] - spn[g] : 0.f;
+        for (int k = 0; k < CPL; ++k) {
+          wo[(wave * G + g) * 2 * D + dblk * CPL + k] = o[g][k];
+          wo[(wave * G + g) * 2 * D + D + dblk * CPL + k] = QJLV ? 2.f * acc[g][k] - spn[g] : 0.f;
         }
     }
     if (lane == 0) {

@@ -13,11 +13,26 @@
 // last level lane k holds the full scores of one row, which feed the shared
 // softmax and the matrix-core P.V tail (values in 32-token tiles).  Queries are
 // applied as a log2-domain softmax scale.
+#include <type_traits>
+
 #include "mfma_pv.hpp"
 
 namespace pgkq {
 
 namespace {
+
+// f(integral_constant<int, I>) for I = B .. E - 1, so that array indices derived
+// from I are compile-time constants however large the unrolled body grows
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// number of trailing one bits of i, at most cap
+constexpr int trailing_ones(int i, int cap) { return (cap > 0 && (i & 1)) ? 1 + trailing_ones(i >> 1, cap - 1) : 0; }
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -112,9 +127,9 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
     // soon as both halves of a level exist: at most LEVELS + 1 live per head
     float part[G][LEVELS + 1];
     float s[G];
-#pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      if (kSplitK && it == KROWS) {
+    static_for<0, NIT>([&](auto itc) {
+      constexpr int it = decltype(itc)::value;
+      if constexpr (kSplitK && it == KROWS) {
         sched_fence();
 #pragma unroll
         for (int r = 0; r < KROWS; ++r)
@@ -132,30 +147,26 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
         for (int g = 0; g < G; ++g) dot[g] = fmaf(f.y, qr[g][2 * j + 1], fmaf(f.x, qr[g][2 * j], dot[g]));
       }
       // carry the new leaf up the tree: level L combines when bit L of it
-      // completes a pair of blocks
+      // completes a pair of blocks, i.e. for the trailing one bits of it
+      constexpr int TOP = trailing_ones(it, LEVELS);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float v = dot[g];
-        int lvl = 0;
-#pragma unroll
-        for (int L = 0; L < LEVELS; ++L) {
-          if (lvl == L && ((it >> L) & 1)) {
-            const bool keep_hi = (kb >> L) & 1;
-            const float lo = part[g][L], hi = v;
-            const float keep = keep_hi ? hi : lo;
-            const float send = keep_hi ? lo : hi;
-            const float recv = L == 0 ? dpp_partner<0>(send)
-                             : L == 1 ? dpp_partner<1>(send)
-                             : L == 2 ? dpp_partner<2>(send)
-                                      : dpp_partner<3>(send);
-            v = keep + recv;
-            lvl = L + 1;
-          }
+        static_for<0, TOP>([&](auto lc) {
+          constexpr int L = decltype(lc)::value;
+          const bool keep_hi = (kb >> L) & 1;
+          const float lo = part[g][L], hi = v;
+          const float keep = keep_hi ? hi : lo;
+          const float send = keep_hi ? lo : hi;
+          v = keep + dpp_partner<L>(send);
+        });
+        if constexpr (TOP < LEVELS) {
+          part[g][TOP] = v;
+        } else {
+          s[g] = v;
         }
-        if (lvl < LEVELS) part[g][lvl] = v;
-        else s[g] = v;
       }
-    }
+    });
     if constexpr (kSplitK) {
       sched_fence();  // keep the value loads behind the key registers' last use
       sm.load_v(vc, c0, vrs, t_end);

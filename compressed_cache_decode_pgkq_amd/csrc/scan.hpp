@@ -197,6 +197,10 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   constexpr int NC = N * P / 32;
   constexpr int NW = NC + M / 32;
   constexpr int NQT = QJL ? (M / 4) * 16 * G : 1;
+  // table lookups per scheduling group: at most 32 table floats in flight (16
+  // with coded values for 8 heads, whose accumulators take more registers)
+  constexpr int PG_FLOATS = CODED_V && G >= 8 ? 16 : 32;
+  constexpr int PG = kPairGroup * G <= PG_FLOATS ? kPairGroup : (PG_FLOATS / G > 0 ? PG_FLOATS / G : 1);
   constexpr int MERGE_FLOATS = VP::MERGE_FLOATS;
   constexpr int MAIN_FLOATS = SS::TABLE_FLOATS > MERGE_FLOATS ? SS::TABLE_FLOATS : MERGE_FLOATS;
   (void)BA;
@@ -351,13 +355,13 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       // bound the work in flight (registers): the code words of each group of
-      // 8 pairs are pinned at the group's start, so neither their bit-field
+      // PG pairs are pinned at the group's start, so neither their bit-field
       // extracts nor their table reads are hoisted above it
-      if ((i % kPairGroup) == 0) {
+      if ((i % PG) == 0) {
 #pragma unroll
         for (int g = 0; g < G; ++g) pin_reg(s[g]);
 #pragma unroll
-        for (int w = (P * i) / 32; w <= (P * (i + kPairGroup) - 1) / 32 && w < NC; ++w) pin_reg(cw[w]);
+        for (int w = (P * i) / 32; w <= (P * (i + PG) - 1) / 32 && w < NC; ++w) pin_reg(cw[w]);
       }
       const uint32_t code = code_at<P>(cw, i);
       float e[G];
@@ -378,7 +382,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       for (int g = 0; g < G; ++g) qs[g] = 0.f;
 #pragma unroll
       for (int k = 0; k < M / 4; ++k) {
-        if ((k % kPairGroup) == 0) {
+        if ((k % PG) == 0) {
 #pragma unroll
           for (int g = 0; g < G; ++g) pin_reg(qs[g]);
           pin_reg(cw[NC + (k >> 3)]);

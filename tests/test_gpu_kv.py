@@ -144,6 +144,20 @@ def test_kv_group_sizes(group):
     assert err <= OUT_TOL, err
 
 
+@pytest.mark.parametrize("base,bm_v", [("nano_b64_t512", 3), ("nano_b64_t512_b4", 4),
+                                       ("gqa_b16_t32k", 2), ("gqa_b1_t131k", 4)])
+def test_kv_eight_heads_per_kv_head(base, bm_v):
+    """8 query heads per kv-head: a lane holds 4 value channels instead of 8
+    (d64 and d128, with and without the sketch, value widths 2 to 4), several
+    splits and a ragged length."""
+    cfg = CONFIGS[base].with_(n_seq=1, n_kv=2, n_q=16, n_tokens=450)
+    case = KVCase(cfg, bm_v)
+    want = case.oracle_out()
+    for ns in (0, 1, 5):
+        err = float(np.abs(case.gpu_decode(ns) - want).max())
+        assert err <= OUT_TOL, (base, bm_v, ns, err)
+
+
 @pytest.mark.parametrize("T", [1, 63, 65, 777])
 def test_kv_ragged_lengths(T):
     case = KVCase(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=1000), 3, n_tokens=T, capacity=1024)
