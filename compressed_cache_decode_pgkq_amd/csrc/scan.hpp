@@ -266,6 +266,38 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
 
   if constexpr (FUSED) fp.run(a, b, h, tid);
 
+  // Token ranges: either the workgroup's split is shared by its wavefronts in
+  // interleaved chunks, or (wave_parts) every wavefront scans a contiguous
+  // partition of it; either way the wavefronts are merged in the workgroup.
+  int64_t c_first, c_end, c_step;
+  if (a.wave_parts) {
+    const int64_t tpw = a.tokens_per_split / kScanWaves;
+    c_first = t_begin + int64_t(wave) * tpw;
+    c_end = min<int64_t>(c_first + tpw, t_end);
+    c_step = kWave;
+  } else {
+    c_first = t_begin + int64_t(wave) * kWave;
+    c_end = t_end;
+    c_step = kScanThreads;
+  }
+  // With the query prepared here (one workgroup per stream, a long prologue)
+  // the first chunk's loads are issued before the tables are built; with the
+  // split launch this measured slower (more registers live in the prologue).
+  constexpr bool EARLY = FUSED;
+  auto issue = [&](int64_t c0) {
+    load_codes(c0);
+    if constexpr (!LOGITS) {
+      if constexpr (CODED_V) {
+        sm.load_v(vc, c0, vrs);
+      } else {
+        sm.load_v(vc, c0, vrs, t_end);
+      }
+    }
+  };
+  if constexpr (EARLY) {
+    if (c_first < c_end) issue(c_first);
+  }
+
   // ---- tables: one thread per (pair, query head)
   {
     float lvr[L];
@@ -323,31 +355,10 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   }
   __syncthreads();
 
-  // Token ranges: either the workgroup's split is shared by its wavefronts in
-  // interleaved chunks, or (wave_parts) every wavefront scans a contiguous
-  // partition of it; either way the wavefronts are merged in the workgroup.
-  int64_t c_first, c_end, c_step;
-  if (a.wave_parts) {
-    const int64_t tpw = a.tokens_per_split / kScanWaves;
-    c_first = t_begin + int64_t(wave) * tpw;
-    c_end = min<int64_t>(c_first + tpw, t_end);
-    c_step = kWave;
-  } else {
-    c_first = t_begin + int64_t(wave) * kWave;
-    c_end = t_end;
-    c_step = kScanThreads;
-  }
   for (int64_t c0 = c_first; c0 < c_end; c0 += c_step) {
     const int64_t t = c0 + lane;
     const bool valid = t < c_end;
-    load_codes(c0);
-    if constexpr (!LOGITS) {
-      if constexpr (CODED_V) {
-        sm.load_v(vc, c0, vrs);
-      } else {
-        sm.load_v(vc, c0, vrs, t_end);
-      }
-    }
+    if (!EARLY || c0 != c_first) issue(c0);
 
     float s[G];
 #pragma unroll
