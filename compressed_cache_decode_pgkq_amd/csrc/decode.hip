@@ -9,7 +9,8 @@
 // Three kernels on one stream:
 //   query_prep   per (sequence, query head): q~ = H (signs * q[perm]) / sqrt(d),
 //                the per-pair angle table q~[2i] cos(c_a) + q~[2i+1] sin(c_a) for
-//                every angle code a, and S_h q~ for the QJL term;
+//                every angle code a, and S_h q~ for the QJL term (done inside
+//                the scan when each stream is one workgroup and G <= 2);
 //   decode_scan  per (sequence, kv-head, token split): builds in LDS, for the G
 //                query heads sharing the kv-head, a joint table indexed by the
 //                pair's (radius, angle) code, J[i][code][g] = level[rc] *
@@ -18,8 +19,8 @@
 //                nibble sums of kappa * S_h q~ for the sketch.  Lane = token for
 //                the score: one coalesced dword load per code word, one LDS read
 //                per pair giving all G heads, one per sketch nibble.  Online
-//                softmax per wavefront, then lane = 8 channels of a token for
-//                the P.V accumulation (16-byte fp16 V loads, fp32 accumulate);
+//                softmax per wavefront; the weighted sum of the fp16 values on
+//                the matrix cores over the value cache in 32-token tiles;
 //   merge        log-sum-exp merge of the split partial states.
 #include "scan.hpp"
 
