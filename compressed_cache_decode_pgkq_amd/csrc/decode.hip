@@ -144,9 +144,12 @@ constexpr int kPrepThreads = 256;
 // One workgroup per query head: q~ = H (signs * q[perm]) / sqrt(d), the
 // per-pair angle table q~[2i] cos thetahat_a + q~[2i+1] sin thetahat_a and,
 // with QJL, S_h q~.  The kernel is latency-bound, so every global load that
-// does not depend on another is issued at the start: the thread's slice of a
-// row of S_h (kept in registers), the query row, the signs and the channel
-// order (the permuted gather then reads the query row from LDS).
+// does not depend on another is issued at the start: S_h, the query row, the
+// signs and the channel order (the permuted gather then reads the query row
+// from LDS).  S_h is read with coalesced 16-byte loads (a wave instruction
+// covers 1 KiB of consecutive floats) and staged in LDS, one padded segment
+// per thread holding the contiguous slice of a row that thread multiplies;
+// loading those slices directly would touch 64 cache lines per instruction.
 template <int D, int BM, bool QJL>
 __global__ void __launch_bounds__(kPrepThreads)
 query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
@@ -167,12 +170,19 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
   // decode step: the first query head of each kv-head appends its new token
   if (a.append_slot >= 0 && hq % a.group == 0) append_key<D, BM, QJL>(a, S, b, h, tid);
 
-  float4 srow[QJL ? CPT / 4 : 1];
+  // thread tid multiplies floats [tid CPT, (tid + 1) CPT) of S_h (row tid / TPR,
+  // slice tid % TPR); they sit in LDS segment tid, padded by 16 bytes so that
+  // the segments' 16-byte reads fall in distinct banks
+  constexpr int SEG = CPT + 4;
+  constexpr int SLD = QJL ? M * D / 4 / kPrepThreads : 1;  // float4 loads per thread
+  static_assert(!QJL || (M * D) % (4 * kPrepThreads) == 0, "S_h tiling");
+  __shared__ __align__(16) float s_S[QJL ? kPrepThreads * SEG : 4];
+  float4 sld[SLD];
   const int r = tid / TPR, part = tid % TPR;
   if constexpr (QJL) {
-    const float4* Sr = reinterpret_cast<const float4*>(S + (size_t(h) * M + r) * D + part * CPT);
+    const float4* Sh = reinterpret_cast<const float4*>(S + size_t(h) * M * D);
 #pragma unroll
-    for (int k = 0; k < CPT / 4; ++k) srow[k] = Sr[k];
+    for (int j = 0; j < SLD; ++j) sld[j] = Sh[tid + kPrepThreads * j];
   }
   __shared__ float sraw[D];
   __shared__ float sx[D];
@@ -188,6 +198,13 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
   // the angle code tid % A)
   double acs, asn;
   sincospi(-1.0 + (2.0 * (tid % A) + 1.0) / double(A), &asn, &acs);
+  if constexpr (QJL) {
+#pragma unroll
+    for (int j = 0; j < SLD; ++j) {
+      const int o = 4 * (tid + kPrepThreads * j);  // float offset in S_h
+      *reinterpret_cast<float4*>(&s_S[(o / CPT) * SEG + o % CPT]) = sld[j];
+    }
+  }
   __syncthreads();
   if (tid < D) sx[tid] = sraw[src] * sgn;
   __syncthreads();
@@ -227,10 +244,11 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
 #pragma unroll
     for (int k = 0; k < CPT / 4; ++k) {
       const int c = part * CPT + 4 * k;
-      acc = fma(double(srow[k].x), sq64[c], acc);
-      acc = fma(double(srow[k].y), sq64[c + 1], acc);
-      acc = fma(double(srow[k].z), sq64[c + 2], acc);
-      acc = fma(double(srow[k].w), sq64[c + 3], acc);
+      const float4 v = *reinterpret_cast<const float4*>(&s_S[tid * SEG + 4 * k]);
+      acc = fma(double(v.x), sq64[c], acc);
+      acc = fma(double(v.y), sq64[c + 1], acc);
+      acc = fma(double(v.z), sq64[c + 2], acc);
+      acc = fma(double(v.w), sq64[c + 3], acc);
     }
     acc += quad_xor<1>(acc);
     if constexpr (TPR == 4) acc += quad_xor<2>(acc);
