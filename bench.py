@@ -217,6 +217,33 @@ def run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E, reps: in
     return res
 
 
+def run_decode_step(api, torch, dev, cfg, p, q, K, V, codes, Vt, signs, perm, cb, S, ws, flush, E,
+                    reps: int = 20):
+    """The fused append + decode step on the main workload: the token of slot
+    T - 1 is encoded and written again (same key and value rows), then
+    attention runs over the T cached tokens; whole call, caches evicted
+    before each call."""
+    n_seq, n_kv, T, d = K.shape
+    k_new = K[:, :, T - 1].contiguous()
+    v_new = V[:, :, T - 1].contiguous()
+    out = torch.empty((n_seq, cfg.n_q, d), dtype=torch.float32, device=dev)
+    c0, c1 = E(), E()
+    ts = []
+    for r in range(reps + 3):
+        flush.fill_(r & 255)
+        c0.record()
+        api.pgkq_decode_step(p, q, k_new, v_new, codes, Vt, T - 1, signs, perm, cb, S,
+                             n_splits=cfg.n_splits, out=out, workspace=ws)
+        c1.record()
+        torch.cuda.synchronize()
+        if r >= 3:
+            ts.append(c0.elapsed_time(c1))
+    ms = float(np.median(ts))
+    return {"description": "append one token per stream (encode its key, write its value) and "
+                           "decode over the 32768 cached tokens, one call",
+            "call_ms": ms, "cache_tokens_per_s": n_seq * T / (ms * 1e-3)}
+
+
 def run_other_workloads(api, torch, dev, flush, E, reps: int = 20):
     """Decode of the other configurations of the pages' workload list on this
     GPU (NanoGPT-256 context with and without QJL, the 131k-token single
@@ -374,6 +401,8 @@ def main():
     pct = lambda k: {"p10": float(np.percentile(ph[:, k], 10)), "p50": float(np.median(ph[:, k])),  # noqa: E731
                      "p90": float(np.percentile(ph[:, k], 90))}
     copy_gbs = measure_copy(torch, dev)
+    step_res = run_decode_step(api, torch, dev, cfg, p, q, K, V, codes, Vt, signs, perm, cb, S, ws,
+                               flush, E)
     controls = run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E)
     others = run_other_workloads(api, torch, dev, flush, E)
 
@@ -450,6 +479,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean,
                      "measured_copy_gbs": copy_gbs},
+        "decode_step": step_res,
         "controls": controls,
         "other_workloads": others,
     }

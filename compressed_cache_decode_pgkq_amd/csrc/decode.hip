@@ -28,17 +28,64 @@ namespace pgkq {
 
 namespace {
 
+constexpr int kPrepThreads = 256;
+
+// S_h staged in LDS for the per-thread products with S_h (S_h q~ in the query
+// preparation, S_h eps~ in the append): thread t multiplies floats
+// [t CPT, (t + 1) CPT) of S_h (row t / TPR, slice t % TPR), which sit in LDS
+// segment t, padded by 16 bytes so that the segments' 16-byte reads fall in
+// distinct banks.  S_h is read with coalesced 16-byte loads (a wave
+// instruction covers 1 KiB of consecutive floats); loading each thread's
+// contiguous slice directly would touch 64 cache lines per instruction.
+template <int D, bool QJL>
+struct SStage {
+  static constexpr int M = QJL ? D : 0;
+  static constexpr int TPR = QJL ? kPrepThreads / D : 1;  // threads per row of S_h
+  static constexpr int CPT = D / TPR;                      // columns per thread
+  static constexpr int SEG = CPT + 4;
+  static constexpr int SLD = QJL ? M * D / 4 / kPrepThreads : 1;  // float4 loads per thread
+  static constexpr int FLOATS = QJL ? kPrepThreads * SEG : 4;
+  static_assert(!QJL || TPR == 2 || TPR == 4, "rows of S_h per workgroup");
+  static_assert(!QJL || (M * D) % (4 * kPrepThreads) == 0, "S_h tiling");
+  typedef float4 Loads[SLD];
+
+  __device__ __forceinline__ static void load(Loads& v, const float* __restrict__ S, int h, int tid) {
+    if constexpr (QJL) {
+      const float4* Sh = reinterpret_cast<const float4*>(S + size_t(h) * M * D);
+#pragma unroll
+      for (int j = 0; j < SLD; ++j) v[j] = Sh[tid + kPrepThreads * j];
+    }
+  }
+  // the caller synchronizes the workgroup before the segments are read
+  __device__ __forceinline__ static void store(const Loads& v, float* s_S, int tid) {
+    if constexpr (QJL) {
+#pragma unroll
+      for (int j = 0; j < SLD; ++j) {
+        const int o = 4 * (tid + kPrepThreads * j);  // float offset in S_h
+        *reinterpret_cast<float4*>(&s_S[(o / CPT) * SEG + o % CPT]) = v[j];
+      }
+    }
+  }
+  __device__ __forceinline__ static float4 slice(const float* s_S, int tid, int k) {
+    return *reinterpret_cast<const float4*>(&s_S[tid * SEG + 4 * k]);
+  }
+};
+
 // ------------------------------------------------------------------ append
 
 // Encode one new key of stream (b, h) into slot a.append_slot and copy its
-// value row: steps (1)-(4) of the pipeline for a single key, by the threads
-// of a query-prep workgroup (at least d of them).  Decisions are taken on the unnormalized
-// transform X = sqrt(d) k~ (exact in float64 for fp16 keys): X_x^2 + X_y^2
-// against d T_j^2 and the octant comparisons of (X_x, X_y), as in the bulk
-// encoder; the residual, its norm and the QJL projection are float64.
+// value row: steps (1)-(4) of the pipeline for a single key, by the
+// kPrepThreads threads of a workgroup of the preparation launch.  Decisions
+// are taken on the unnormalized transform X = sqrt(d) k~ (exact in float64 for
+// fp16 keys): X_x^2 + X_y^2 against d T_j^2 and the octant comparisons of
+// (X_x, X_y), as in the bulk encoder; the residual, its norm and the QJL
+// projection are float64 (each thread's slice of a row of S_h, the slices
+// summed by DPP exchanges).  `sv` holds this thread's coalesced loads of S_h,
+// staged into s_S with the key row.
 template <int D, int BM, bool QJL>
-__device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int64_t b, int h,
-                           int tid) {
+__device__ __forceinline__ void append_key(const DecodeArgs& a, int64_t b, int h, int tid,
+                           const typename SStage<D, QJL>::Loads& sv, float* s_S) {
+  using ST = SStage<D, QJL>;
   constexpr int N = D / 2;
   constexpr int BA = BM - 1;
   constexpr int P = BM + BA;
@@ -47,36 +94,52 @@ __device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int
   constexpr int M = QJL ? D : 0;
   constexpr int NC = N * P / 32;
   constexpr int NSW = M / 32;
+  static_assert(D / 2 <= kWave, "one wavefront holds a level's butterflies");
+  __shared__ float s_raw[D];
+  __shared__ float s_cb[2 * L];
+  __shared__ double2 s_grid[A];  // (cos, sin) of the angle grid
   __shared__ double s_x[D];
   __shared__ double s_ss[N];
   __shared__ uint32_t s_code[N];
   __shared__ uint32_t s_bit[D];
   const int64_t stream = b * a.n_kv + h;
-  const float* cb = a.codebook + size_t(h) * 2 * L;
+  // independent loads first: the key row as stored, the value row, the channel
+  // order, the signs and the codebook (the permuted gather then reads the row
+  // from LDS); the angle grid is computed meanwhile
+  int src = tid;
+  bool neg = false;
+  __half vrow = __float2half(0.f);
   if (tid < D) {
-    const int src = a.perm ? int(a.perm[size_t(h) * D + tid]) : tid;
-    double v = static_cast<double>(load_f(a.k_new, a.k_dtype, size_t(stream) * D + src));
-    if (a.hadamard && a.signs[size_t(h) * D + tid] < 0) v = -v;
-    s_x[tid] = v;
+    s_raw[tid] = load_f(a.k_new, a.k_dtype, size_t(stream) * D + tid);
+    vrow = a.v_new[size_t(stream) * D + tid];
+    if (a.perm) src = int(a.perm[size_t(h) * D + tid]);
+    neg = a.hadamard && a.signs[size_t(h) * D + tid] < 0;
+  }
+  if (tid < 2 * L) s_cb[tid] = a.codebook[size_t(h) * 2 * L + tid];
+  if (QJL && tid < A) {
+    double sn, cs;
+    sincospi(-1.0 + (2.0 * tid + 1.0) / double(A), &sn, &cs);
+    s_grid[tid] = make_double2(cs, sn);
+  }
+  ST::store(sv, s_S, tid);  // S_h arrives with the key; staged before the transform
+  __syncthreads();
+  if (tid < D) {
+    const double v = static_cast<double>(s_raw[src]);
+    s_x[tid] = neg ? -v : v;
   }
   __syncthreads();
-  if (a.hadamard) {
+  if (a.hadamard && tid < kWave) {  // every butterfly of a level sits in wavefront 0
     for (int hh = 1; hh < D; hh <<= 1) {
-      double u = 0.0, w = 0.0;
-      int c0 = 0;
       if (tid < D / 2) {
-        c0 = (tid / hh) * 2 * hh + (tid % hh);
-        u = s_x[c0];
-        w = s_x[c0 + hh];
-      }
-      __syncthreads();
-      if (tid < D / 2) {
+        const int c0 = (tid / hh) * 2 * hh + (tid % hh);
+        const double u = s_x[c0], w = s_x[c0 + hh];
         s_x[c0] = u + w;
         s_x[c0 + hh] = u - w;
       }
-      __syncthreads();
+      wave_lds_sync();  // the next level reads what other lanes wrote
     }
   }
+  __syncthreads();
   if (tid < N) {
     const double x = s_x[2 * tid], y = s_x[2 * tid + 1];
     const double r2 = x * x + y * y;
@@ -84,18 +147,17 @@ __device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int
     int rc = 0;
 #pragma unroll
     for (int j = 0; j < L - 1; ++j) {
-      const double t = static_cast<double>(cb[L + j]);
+      const double t = static_cast<double>(s_cb[L + j]);
       rc += (tscale * t * t < r2) ? 1 : 0;
     }
     const int ac = octant_cell(x, y) >> (3 - BA);
     s_code[tid] = static_cast<uint32_t>(rc | (ac << BM));
     if constexpr (QJL) {
       const double inv_scale = a.hadamard ? 1.0 / sqrt(double(D)) : 1.0;
-      double sn, cs;
-      sincospi(-1.0 + (2.0 * ac + 1.0) / double(A), &sn, &cs);
-      const double lv = static_cast<double>(cb[rc]);
-      const double ex = x * inv_scale - lv * cs;
-      const double ey = y * inv_scale - lv * sn;
+      const double2 cs = s_grid[ac];
+      const double lv = static_cast<double>(s_cb[rc]);
+      const double ex = x * inv_scale - lv * cs.x;
+      const double ey = y * inv_scale - lv * cs.y;
       s_x[2 * tid] = ex;   // this thread's own pair: no other reader yet
       s_x[2 * tid + 1] = ey;
       s_ss[tid] = ex * ex + ey * ey;
@@ -103,12 +165,20 @@ __device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int
   }
   __syncthreads();
   if constexpr (QJL) {
-    if (tid < M) {
-      const float* Sr = S + (size_t(h) * M + tid) * D;
-      double u = 0.0;
-      for (int c = 0; c < D; ++c) u += static_cast<double>(Sr[c]) * s_x[c];
-      s_bit[tid] = u >= 0.0 ? 1u : 0u;
+    const int r = tid / ST::TPR, part = tid % ST::TPR;
+    double u = 0.0;
+#pragma unroll
+    for (int k = 0; k < ST::CPT / 4; ++k) {
+      const int c = part * ST::CPT + 4 * k;
+      const float4 v = ST::slice(s_S, tid, k);
+      u = fma(double(v.x), s_x[c], u);
+      u = fma(double(v.y), s_x[c + 1], u);
+      u = fma(double(v.z), s_x[c + 2], u);
+      u = fma(double(v.w), s_x[c + 3], u);
     }
+    u += quad_xor<1>(u);
+    if constexpr (ST::TPR == 4) u += quad_xor<2>(u);
+    if (part == 0) s_bit[r] = u >= 0.0 ? 1u : 0u;
     __syncthreads();
   }
   const int64_t slot = a.append_slot;
@@ -134,56 +204,47 @@ __device__ void append_key(const DecodeArgs& a, const float* __restrict__ S, int
     nu[slot] = f64_to_f16_rne_sat_nonneg(sqrt(ss));
   }
   if (tid < D)  // the value row goes into the stream's 32-token tiles
-    a.V_w[size_t(stream) * a.capacity * D + vtile_index(slot, tid, D)] = a.v_new[size_t(stream) * D + tid];
+    a.V_w[size_t(stream) * a.capacity * D + vtile_index(slot, tid, D)] = vrow;
 }
 
 // ------------------------------------------------------------------ query prep
 
-constexpr int kPrepThreads = 256;
-
 // One workgroup per query head: q~ = H (signs * q[perm]) / sqrt(d), the
 // per-pair angle table q~[2i] cos thetahat_a + q~[2i+1] sin thetahat_a and,
 // with QJL, S_h q~.  The kernel is latency-bound, so every global load that
-// does not depend on another is issued at the start: S_h, the query row, the
-// signs and the channel order (the permuted gather then reads the query row
-// from LDS).  S_h is read with coalesced 16-byte loads (a wave instruction
-// covers 1 KiB of consecutive floats) and staged in LDS, one padded segment
-// per thread holding the contiguous slice of a row that thread multiplies;
-// loading those slices directly would touch 64 cache lines per instruction.
+// does not depend on another is issued at the start: S_h (staged in LDS,
+// SStage), the query row, the signs and the channel order (the permuted gather
+// then reads the query row from LDS).  For a decode step the launch has one
+// more workgroup per (sequence, kv-head), which appends the stream's new token
+// beside the preparation instead of before it.
 template <int D, int BM, bool QJL>
 __global__ void __launch_bounds__(kPrepThreads)
 query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
+  using ST = SStage<D, QJL>;
   constexpr int N = D / 2;
   constexpr int BA = BM - 1;
   constexpr int A = 1 << BA;
-  constexpr int M = QJL ? D : 0;
-  constexpr int TPR = QJL ? kPrepThreads / (QJL ? M : 1) : 1;  // threads per row of S_h
-  constexpr int CPT = D / TPR;                                  // columns per thread
-  static_assert(!QJL || (TPR == 2 || TPR == 4), "rows of S_h per workgroup");
+  constexpr int M = ST::M;
+  constexpr int TPR = ST::TPR;
+  constexpr int CPT = ST::CPT;
   static_assert(kPrepThreads % A == 0 && kPrepThreads >= D, "thread mapping");
   const PrepLayout pl{D, N, A, M};
   const int tid = threadIdx.x;
   const int hq = blockIdx.x;
   const int64_t b = blockIdx.y;
-  const int h = hq / a.group;
+  __shared__ __align__(16) float s_S[ST::FLOATS];
 
-  // decode step: the first query head of each kv-head appends its new token
-  if (a.append_slot >= 0 && hq % a.group == 0) append_key<D, BM, QJL>(a, S, b, h, tid);
-
-  // thread tid multiplies floats [tid CPT, (tid + 1) CPT) of S_h (row tid / TPR,
-  // slice tid % TPR); they sit in LDS segment tid, padded by 16 bytes so that
-  // the segments' 16-byte reads fall in distinct banks
-  constexpr int SEG = CPT + 4;
-  constexpr int SLD = QJL ? M * D / 4 / kPrepThreads : 1;  // float4 loads per thread
-  static_assert(!QJL || (M * D) % (4 * kPrepThreads) == 0, "S_h tiling");
-  __shared__ __align__(16) float s_S[QJL ? kPrepThreads * SEG : 4];
-  float4 sld[SLD];
-  const int r = tid / TPR, part = tid % TPR;
-  if constexpr (QJL) {
-    const float4* Sh = reinterpret_cast<const float4*>(S + size_t(h) * M * D);
-#pragma unroll
-    for (int j = 0; j < SLD; ++j) sld[j] = Sh[tid + kPrepThreads * j];
+  if (hq >= a.n_q) {  // decode step: the appending workgroup of kv-head hq - n_q
+    const int h = hq - int(a.n_q);
+    typename ST::Loads sv;
+    ST::load(sv, S, h, tid);
+    append_key<D, BM, QJL>(a, b, h, tid, sv, s_S);
+    return;
   }
+  const int h = hq / a.group;
+  const int r = tid / TPR, part = tid % TPR;
+  typename ST::Loads sv;
+  ST::load(sv, S, h, tid);
   __shared__ float sraw[D];
   __shared__ float sx[D];
   __shared__ double sq64[D];
@@ -198,33 +259,23 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
   // the angle code tid % A)
   double acs, asn;
   sincospi(-1.0 + (2.0 * (tid % A) + 1.0) / double(A), &asn, &acs);
-  if constexpr (QJL) {
-#pragma unroll
-    for (int j = 0; j < SLD; ++j) {
-      const int o = 4 * (tid + kPrepThreads * j);  // float offset in S_h
-      *reinterpret_cast<float4*>(&s_S[(o / CPT) * SEG + o % CPT]) = sld[j];
-    }
-  }
+  ST::store(sv, s_S, tid);
   __syncthreads();
   if (tid < D) sx[tid] = sraw[src] * sgn;
   __syncthreads();
-  if (a.hadamard) {
+  static_assert(N <= kWave, "one wavefront holds a level's butterflies");
+  if (a.hadamard && tid < kWave) {  // every butterfly of a level sits in wavefront 0
     for (int hh = 1; hh < D; hh <<= 1) {
-      float u = 0.f, w = 0.f;
-      int c0 = 0;
       if (tid < N) {
-        c0 = (tid / hh) * 2 * hh + (tid % hh);
-        u = sx[c0];
-        w = sx[c0 + hh];
-      }
-      __syncthreads();
-      if (tid < N) {
+        const int c0 = (tid / hh) * 2 * hh + (tid % hh);
+        const float u = sx[c0], w = sx[c0 + hh];
         sx[c0] = u + w;
         sx[c0 + hh] = u - w;
       }
-      __syncthreads();
+      wave_lds_sync();  // the next level reads what other lanes wrote
     }
   }
+  __syncthreads();
   float* out = a.prep + (size_t(b) * a.n_q + hq) * pl.stride();
   const float sc = a.hadamard ? 1.0f / sqrtf(float(D)) : 1.0f;
   if (tid < D) {
@@ -244,7 +295,7 @@ query_prep_kernel(DecodeArgs a, const float* __restrict__ S) {
 #pragma unroll
     for (int k = 0; k < CPT / 4; ++k) {
       const int c = part * CPT + 4 * k;
-      const float4 v = *reinterpret_cast<const float4*>(&s_S[tid * SEG + 4 * k]);
+      const float4 v = ST::slice(s_S, tid, k);
       acc = fma(double(v.x), sq64[c], acc);
       acc = fma(double(v.y), sq64[c + 1], acc);
       acc = fma(double(v.z), sq64[c + 2], acc);
@@ -350,7 +401,9 @@ __global__ void __launch_bounds__(kMergeThreads) merge_kernel(const float* __res
 
 template <int D, int BM, bool QJL>
 hipError_t prep_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((query_prep_kernel<D, BM, QJL>), dim3(unsigned(a.n_q), unsigned(a.n_seq)),
+  // a decode step adds one appending workgroup per (sequence, kv-head)
+  const int64_t nx = a.n_q + (a.append_slot >= 0 ? a.n_kv : 0);
+  hipLaunchKernelGGL((query_prep_kernel<D, BM, QJL>), dim3(unsigned(nx), unsigned(a.n_seq)),
                      dim3(kPrepThreads), 0, s, a, a.S);
   return hipGetLastError();
 }
