@@ -118,7 +118,22 @@ struct FusedPrep {
       }
       __syncthreads();
     }
-    if (a.hadamard) {
+    if constexpr (G * N <= kWave) {
+      // every butterfly of a level sits in wavefront 0: no workgroup barriers
+      if (a.hadamard && tid < kWave) {
+        for (int hh = 1; hh < D; hh <<= 1) {
+          if (tid < G * N) {
+            const int g = tid / N, j = tid % N;
+            const int at = g * D + (j / hh) * 2 * hh + (j % hh);
+            const float u = (&qf[0][0])[at], w = (&qf[0][0])[at + hh];
+            (&qf[0][0])[at] = u + w;
+            (&qf[0][0])[at + hh] = u - w;
+          }
+          wave_lds_sync();  // the next level reads what other lanes wrote
+        }
+      }
+      __syncthreads();
+    } else if (a.hadamard) {
       constexpr int BE = (G * N + kScanThreads - 1) / kScanThreads;
       for (int hh = 1; hh < D; hh <<= 1) {
         float u[BE], w[BE];
