@@ -89,11 +89,20 @@ __global__ void __launch_bounds__(D) calib_finalize_kernel(CalibArgs a) {
   __shared__ double s_ss[D];
   __shared__ int s_pi[D];
   __shared__ double s_sigma;
-  // eight interleaved partial sums (independent loads in flight), combined in
-  // a fixed order: the result does not depend on scheduling
+  // eight interleaved partial sums (part[k] takes chunks k, k + 8, k + 16, ...
+  // in order), combined in a fixed order: the result does not depend on
+  // scheduling.  32 rows are requested per round trip (the kernel is bound by
+  // load latency), then added in that order.
   double part[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const double* src = a.partial + size_t(h) * a.n_chunks * D + c;
   int64_t ch = 0;
+  for (; ch + 32 <= a.n_chunks; ch += 32) {
+    double v[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) v[k] = src[(ch + k) * D];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) part[k % 8] += v[k];
+  }
   for (; ch + 8 <= a.n_chunks; ch += 8) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) part[k] += src[(ch + k) * D];
