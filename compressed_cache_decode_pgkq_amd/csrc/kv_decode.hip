@@ -5,7 +5,8 @@
 //
 // Two kernels after the shared query preparation:
 //   decode_scan_kernel<..., VB>  the scan of scan.hpp with the coded value path
-//                                (CodedPV): per wavefront a partial state
+//                                (CodedPV): per workgroup (its wavefronts
+//                                merged in LDS) a partial state
 //                                (m, l, o[d], a[d]) with o the weighted pair
 //                                reconstructions and a_j = sum_t p_t nu_t
 //                                (2 bit_tj - 1);

@@ -20,7 +20,8 @@
 //   rtn_scan        the decode scan in the split skeleton of the PGKQ scan:
 //                   lane = token for the score, the query read through the
 //                   scalar cache (wave-uniform), then the shared online softmax
-//                   and fp16 P.V tail.
+//                   and the matrix-core P.V tail over the value cache in
+//                   32-token tiles.
 #include "mfma_pv.hpp"
 
 namespace pgkq {
