@@ -7,19 +7,24 @@
 //     pair's joint code indexes a 2^P-entry LDS table of
 //     (level[rc] cos thetahat[ac], level[rc] sin thetahat[ac]) and is weighted
 //     by p_t;
-//   * QJL part: the same lane owns CPL sketch bits; it accumulates
-//     sum_t p_t nu_t bit_tj and sum_t p_t nu_t, giving
-//     a_j = sum_t p_t nu_t (2 bit_tj - 1).  The product kappa S^T a, linear in
-//     the partial states, is left to the merge kernel (one matrix-vector
-//     product per query head instead of one per partition).
+//   * QJL part: a_j = sum_t p_t nu_t (2 bit_tj - 1) = 2 c_j - s with
+//     c_j = sum_t p_t (bit_tj nu_t) and s = sum_t p_t nu_t.  c is a small
+//     matrix product (G heads x 64 tokens x m sketch columns) and runs on the
+//     matrix cores as v_mfma_f32_16x16x32_f16: A = the weights p split into
+//     fp16 high and low parts (scaled by 2^15, as for fp16 values), B = the
+//     fp16 norm nu_t where bit_tj is set and 0 elsewhere (exact: nu is stored
+//     as fp16), fp32 accumulators; s is summed per token lane.  The product
+//     kappa S^T a, linear in the partial states, is left to the merge kernel
+//     (one matrix-vector product per query head instead of one per
+//     partition).
 // The chunk's code words arrive lane = token (coalesced dword loads) and are
 // transposed through a wave-private LDS block.  The wavefronts' states
 // (m, l, o[d], a[m]) are merged in the workgroup into one partial per split.
-// A lane holds 2 G CPL accumulators: CPL = 8 up to 4 query heads, 4 for 8 heads
-// (twice the rows per lane, half the registers).
+// A lane holds G CPL pair accumulators: CPL = 8 up to 4 query heads, 4 for 8
+// heads (twice the rows per lane, half the registers).
 #pragma once
 
-#include "device_common.hpp"
+#include "mfma_pv.hpp"
 
 namespace pgkq {
 
@@ -35,6 +40,12 @@ struct CodedPV {
   static constexpr int CPL = G >= 8 ? 4 : 8;    // channels per lane
   static constexpr int PPL = CPL / 2;           // pairs per lane
   static constexpr int LPT = D / CPL;           // lanes per token row
+  static constexpr int NSWV = M / 32;           // sketch words per token
+  static constexpr int NB = QJLV ? M / 16 : 1;  // 16-column blocks of the sketch
+  static constexpr int KS = kWave / 32;         // 32-token steps per chunk
+  static constexpr float kPScale = 32768.f;     // 2^15: keeps hi in the normal fp16 range
+  // LDS bytes of one wavefront's sketch weight rows ([hi, lo][G][64] fp16)
+  static constexpr int P16_BYTES = QJLV ? 2 * G * kWave * 2 : 16;
   static constexpr int TPI = kWave / LPT;      // rows per pass
   static constexpr int NIT = kWave / TPI;      // passes per chunk
   static constexpr int WIDTH = 2 * D + 4;      // partial row: m, l, -, -, o[D], a[D]
@@ -46,7 +57,8 @@ struct CodedPV {
   static_assert(PPL * P <= 32, "a lane's pair codes span at most two words");
   static_assert(LPT <= kWave, "lanes per token row");
 
-  float m_run[G], l_lane[G], o[G][CPL], acc[G][CPL], spn[G];
+  float m_run[G], l_lane[G], o[G][CPL], spn[G];
+  f32x4 sacc[NB];  // c of the sketch, C layout of the matrix product (scaled by 2^15)
   int lane, wave, slot, dblk;
   uint32_t row_bytes, nu_off;
 
@@ -68,11 +80,10 @@ struct CodedPV {
       l_lane[g] = 0.f;
       spn[g] = 0.f;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) {
-        o[g][k] = 0.f;
-        acc[g][k] = 0.f;
-      }
+      for (int k = 0; k < CPL; ++k) o[g][k] = 0.f;
     }
+#pragma unroll
+    for (int n = 0; n < NB; ++n) sacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // code words of token c0 + lane (the whole stream is the buffer range;
@@ -85,29 +96,58 @@ struct CodedPV {
   }
 
   // s: raw scores of token c0 + lane; p_rows: the wavefront's [64][G] weights;
-  // vw: its LDS_WORDS transposition block; vtab: the pair table; rows at or
-  // beyond c_end carry no weight.
+  // vw: its LDS_WORDS transposition block; vtab: the pair table; p16: its
+  // P16_BYTES of sketch weight rows; rows at or beyond c_end carry no weight
+  // (their slots may hold any bits).
   __device__ __forceinline__ void chunk(const float (&s)[G], bool valid, float scale_log2,
                                         const VChunk& vc, float* p_rows, uint32_t* vw,
-                                        const float2* vtab, int64_t c0, int64_t c_end) {
-    float pv[G];
+                                        const float2* vtab, int64_t c0, int64_t c_end, void* p16v) {
+    float pv[G], alpha[G];
+    bool grew = false;
+    const float nu_t = QJLV ? half_bits_to_float(static_cast<uint16_t>(vc.nu)) : 0.f;
+    _Float16* p16 = static_cast<_Float16*>(p16v);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float z = valid ? s[g] * scale_log2 : -INFINITY;
       const float mnew = fmaxf(m_run[g], wave_max_uniform(z));
+      alpha[g] = 1.f;
       if (mnew > m_run[g]) {  // wave-uniform
-        const float alpha = fast_exp2(m_run[g] - mnew);
-        l_lane[g] *= alpha;
-        spn[g] *= alpha;
+        alpha[g] = fast_exp2(m_run[g] - mnew);
+        l_lane[g] *= alpha[g];
+        spn[g] *= alpha[g];
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          o[g][k] *= alpha;
-          acc[g][k] *= alpha;
-        }
+        for (int k = 0; k < CPL; ++k) o[g][k] *= alpha[g];
         m_run[g] = mnew;
+        grew = true;
       }
       pv[g] = valid ? fast_exp2(z - m_run[g]) : 0.f;
       l_lane[g] += pv[g];
+      if constexpr (QJLV) {
+        if (valid) spn[g] = fmaf(pv[g], nu_t, spn[g]);
+        const float ps = pv[g] * kPScale;
+        const _Float16 hi = static_cast<_Float16>(ps);
+        const _Float16 lo = static_cast<_Float16>(ps - static_cast<float>(hi));
+        p16[g * kWave + lane] = hi;
+        p16[(G + g) * kWave + lane] = lo;
+      }
+    }
+    if constexpr (QJLV) {
+      if (grew) {  // wave-uniform: rescale the sketch rows of the heads whose maximum grew
+        // lane l holds rows 4(l/16) + r of every block
+        float f[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if constexpr (G <= 4) {
+            f[r] = r < G ? alpha[r] : 1.f;
+          } else {
+            f[r] = (lane >> 4) == 0 ? alpha[r] : ((lane >> 4) == 1 ? alpha[4 + r] : 1.f);
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sacc[n][r] *= f[r];
+      }
     }
     if constexpr (G == 1) {
       p_rows[lane] = pv[0];
@@ -120,7 +160,7 @@ struct CodedPV {
     }
 #pragma unroll
     for (int w = 0; w < NW; ++w) vw[w * VW_STRIDE + lane] = vc.w[w];
-    if constexpr (QJLV) vw[NW * VW_STRIDE + lane] = vc.nu;
+    if constexpr (QJLV) vw[NW * VW_STRIDE + lane] = (c0 + lane < c_end) ? (vc.nu & 0xFFFFu) : 0u;
     wave_lds_sync();
 
     const int o0 = PPL * P * dblk;  // first polar bit of this lane's pairs
@@ -144,21 +184,41 @@ struct CodedPV {
           o[g][2 * j + 1] = fmaf(pp[g], t.y, o[g][2 * j + 1]);
         }
       }
-      if constexpr (QJLV) {
-        constexpr uint32_t smask = (1u << CPL) - 1u;
-        const uint32_t sb =
-            (vw[(NC + (CPL * dblk) / 32) * VW_STRIDE + r] >> ((CPL * dblk) & 31)) & smask;
-        const float nu = half_bits_to_float(static_cast<uint16_t>(vw[NW * VW_STRIDE + r]));
-        const bool live = c0 + r < c_end;  // a slot past the cache may hold any bits
-        float fb[CPL];
+    }
+    if constexpr (QJLV) {
+      // c += P (bit * nu): lane l supplies A[head l % 16][tokens 8 (l / 16) ..]
+      // and B[tokens 8 (l / 16) + j][sketch column 16 n + l % 16]; a token
+      // past c_end has nu = 0 in the block, so its bits do not matter
+      const int arow = (lane & 15) & (G - 1);
+      const int bit = lane & 15;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) fb[k] = static_cast<float>((sb >> k) & 1u);
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r0 = 32 * ks + 8 * (lane >> 4);
+        const f16x8 a_hi = *reinterpret_cast<const f16x8*>(p16 + arow * kWave + r0);
+        const f16x8 a_lo = *reinterpret_cast<const f16x8*>(p16 + (G + arow) * kWave + r0);
+        // nu of tokens (2q, 2q + 1) as one fp16 pair, then per column block a
+        // 0 / -1 mask from each token's bit (sign-extending 1-bit extract)
+        uint32_t nu2[4], sw[8][NSWV];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float pn = live ? pp[g] * nu : 0.f;
-          spn[g] += pn;
+        for (int q = 0; q < 4; ++q)
+          nu2[q] = vw[NW * VW_STRIDE + r0 + 2 * q] | (vw[NW * VW_STRIDE + r0 + 2 * q + 1] << 16);
 #pragma unroll
-          for (int k = 0; k < CPL; ++k) acc[g][k] = fmaf(fb[k], pn, acc[g][k]);
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+          for (int w = 0; w < NSWV; ++w) sw[j][w] = vw[(NC + w) * VW_STRIDE + r0 + j];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const int w = n >> 1, sft = 16 * (n & 1) + bit;
+          u32x4 bq;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t m0 = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(sw[2 * q][w]), sft, 1));
+            const uint32_t m1 = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(sw[2 * q + 1][w]), sft, 1));
+            bq[q] = ((m0 & 0xFFFFu) | (m1 & 0xFFFF0000u)) & nu2[q];
+          }
+          const f16x8 b = __builtin_bit_cast(f16x8, bq);
+          sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b, sacc[n], 0, 0, 0);
+          sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b, sacc[n], 0, 0, 0);
         }
       }
     }
@@ -170,14 +230,9 @@ struct CodedPV {
 #pragma unroll
     for (int off = LPT; off < kWave; off <<= 1) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        spn[g] += __shfl_xor(spn[g], off, kWave);
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          o[g][k] += __shfl_xor(o[g][k], off, kWave);
-          acc[g][k] += __shfl_xor(acc[g][k], off, kWave);
-        }
-      }
+        for (int k = 0; k < CPL; ++k) o[g][k] += __shfl_xor(o[g][k], off, kWave);
     }
   }
 
@@ -189,9 +244,12 @@ struct CodedPV {
   __device__ __forceinline__ void finish(float* scratch, int tid, float* __restrict__ partial,
                                          size_t row0, int split, int n_parts) {
     reduce_slots();
-    float l_w[G];
+    float l_w[G], s_w[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) l_w[g] = wave_sum(l_lane[g]);
+    for (int g = 0; g < G; ++g) {
+      l_w[g] = wave_sum(l_lane[g]);
+      s_w[g] = QJLV ? wave_sum(spn[g]) : 0.f;
+    }
     float* wm = scratch;                  // [WAVES][G]
     float* wl = scratch + WAVES * G;      // [WAVES][G]
     float* wo = scratch + 2 * WAVES * G;  // [WAVES][G][2D]: o, then a
@@ -199,10 +257,17 @@ struct CodedPV {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-          wo[(wave * G + g) * 2 * D + dblk * CPL + k] = o[g][k];
-          wo[(wave * G + g) * 2 * D + D + dblk * CPL + k] = QJLV ? 2.f * acc[g][k] - spn[g] : 0.f;
-        }
+        for (int k = 0; k < CPL; ++k) wo[(wave * G + g) * 2 * D + dblk * CPL + k] = o[g][k];
+    }
+    // a = 2 c - s; lane l holds c of head 4 (l / 16) + r, column 16 n + l % 16
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if ((lane >> 4) == (g >> 2)) {
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+          wo[(wave * G + g) * 2 * D + D + 16 * n + (lane & 15)] =
+              QJLV ? 2.f * (sacc[n][g & 3] * (1.f / kPScale)) - s_w[g] : 0.f;
+      }
     }
     if (lane == 0) {
 #pragma unroll

@@ -229,6 +229,8 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   constexpr int VTAB = CODED_V ? (1 << (2 * VB - 1)) : 1;
   __shared__ __align__(16) uint32_t s_vw[kScanWaves][VW_WORDS];
   __shared__ __align__(16) float2 s_vtab[VTAB];
+  constexpr int P16 = CODED_V ? CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>::P16_BYTES : 16;
+  __shared__ __align__(16) unsigned char s_p16[kScanWaves][P16];
   using FP = FusedPrep<D, BM, QJL, (FUSED ? G : 1)>;
   __shared__ __align__(16) unsigned char s_fused_raw[FUSED ? sizeof(FP) : 16];
   FP& fp = *reinterpret_cast<FP*>(s_fused_raw);
@@ -430,7 +432,8 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
           a.logits[(size_t(b) * a.n_q + size_t(h) * G + g) * a.n_tokens + t] = s[g];
       }
     } else if constexpr (CODED_V) {
-      sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], &s_vw[wave][0], s_vtab, c0, c_end);
+      sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], &s_vw[wave][0], s_vtab, c0, c_end,
+               &s_p16[wave][0]);
     } else {
       sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0]);
     }
