@@ -12,50 +12,89 @@
 //                                (2 bit_tj - 1);
 //   kv_merge_kernel              per (sequence, query head): log-sum-exp merge
 //                                of the partials, then
-//                                out = (o + kappa S_v^T a) / l.
+//                                out = (o + kappa S_v^T a) / l (512 threads:
+//                                groups of d take every J-th partial, then
+//                                d / J rows of S_v each).
 #include "scan.hpp"
 
 namespace pgkq {
 
 namespace {
 
-__global__ void __launch_bounds__(128)
+constexpr int kKvMergeThreads = 512;
+
+// Per (sequence, query head): log-sum-exp merge of the partial states, then
+// out = (o + kappa S_v^T a) / l.  The J = 512 / d thread groups take every
+// J-th partial, and then d / J consecutive rows of S_v each; their sums are
+// combined in LDS in group order (deterministic).  The S_v loads are issued
+// first (they do not depend on the partials): the kernel is bound by latency.
+template <int D>
+__global__ void __launch_bounds__(kKvMergeThreads)
 kv_merge_kernel(const float* __restrict__ partial, float* __restrict__ out, const float* __restrict__ Sv,
-                int d, int n_parts, int group, int qjl) {
+                int n_parts, int group, int qjl) {
+  constexpr int J = kKvMergeThreads / D;  // thread groups
+  constexpr int RPT = D / J;              // rows of S_v per thread
   const int hq = blockIdx.x;
   const int64_t b = blockIdx.y;
   const int nq = gridDim.x;
   const int h = hq / group;
-  const int width = 2 * d + 4;
+  constexpr int width = 2 * D + 4;
   const float* part = partial + (size_t(b) * nq + hq) * size_t(n_parts) * width;
   const int tid = threadIdx.x;
-  __shared__ float s_a[128];
+  const int c = tid % D, j = tid / D;
+  __shared__ float s_num[J][D], s_an[J][D], s_den[J];
+  __shared__ float s_a[D];
+  float sv[RPT];
+  if (qjl) {  // column c of S_v[h], rows [j RPT, (j + 1) RPT)
+    const float* S = Sv + size_t(h) * D * D + size_t(j) * RPT * D + c;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) sv[r] = S[size_t(r) * D];
+  }
   float Mx = -INFINITY;
 #pragma unroll 8
   for (int p = 0; p < n_parts; ++p) Mx = fmaxf(Mx, part[size_t(p) * width]);
   float num = 0.f, an = 0.f, den = 0.f;
-  if (tid < d && Mx != -INFINITY) {
+  if (Mx != -INFINITY) {
 #pragma unroll 4
-    for (int p = 0; p < n_parts; ++p) {
+    for (int p = j; p < n_parts; p += J) {
       const float* pp = part + size_t(p) * width;
       const float f = exp2f(pp[0] - Mx);
-      num += f * pp[4 + tid];
-      an += f * pp[4 + d + tid];
+      num += f * pp[4 + c];
+      an += f * pp[4 + D + c];
       den += f * pp[1];
     }
   }
-  if (tid < d) s_a[tid] = an;
+  s_num[j][c] = num;
+  s_an[j][c] = an;
+  if (c == 0) s_den[j] = den;
   __syncthreads();
-  if (tid < d) {
-    float corr = 0.f;
-    if (qjl) {
-      // kappa S^T a: column tid of S_v[h], rows j < m = d
-      const float* S = Sv + size_t(h) * d * d + tid;
-#pragma unroll 8
-      for (int j = 0; j < d; ++j) corr = fmaf(S[size_t(j) * d], s_a[j], corr);
-      corr *= 1.2533141373155003f / float(d);  // sqrt(pi/2) / m
+  if (j == 0) {
+    float nt = 0.f, at = 0.f, dt = 0.f;
+#pragma unroll
+    for (int k = 0; k < J; ++k) {
+      nt += s_num[k][c];
+      at += s_an[k][c];
+      dt += s_den[k];
     }
-    out[(size_t(b) * nq + hq) * d + tid] = den > 0.f ? (num + corr) / den : 0.f;
+    s_num[0][c] = nt;
+    s_a[c] = at;
+    if (c == 0) s_den[0] = dt;
+  }
+  __syncthreads();
+  float corr = 0.f;
+  if (qjl) {  // this thread's rows of S_v^T a
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) corr = fmaf(sv[r], s_a[j * RPT + r], corr);
+  }
+  s_an[j][c] = corr;  // (every read of s_an precedes the barrier above)
+  __syncthreads();
+  if (j == 0) {
+    float ct = 0.f;
+#pragma unroll
+    for (int k = 0; k < J; ++k) ct += s_an[k][c];
+    ct *= 1.2533141373155003f / float(D);  // kappa = sqrt(pi/2) / m, m = d
+    const float dt = s_den[0];
+    out[(size_t(b) * nq + hq) * D + c] = dt > 0.f ? (s_num[0][c] + ct) / dt : 0.f;
   }
 }
 
@@ -101,9 +140,17 @@ hipError_t launch_kv_decode_scan(const Geometry& g, const DecodeArgs& a, hipStre
 }
 
 hipError_t launch_kv_merge(const DecodeArgs& a, int d, int n_parts, hipStream_t s) {
-  if (d > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_merge_kernel, dim3(unsigned(a.n_q), unsigned(a.n_seq)), dim3(128), 0, s,
-                     a.partial, a.out, a.S_v, d, n_parts, a.group, a.S_v ? 1 : 0);
+  const dim3 grid(static_cast<unsigned>(a.n_q), static_cast<unsigned>(a.n_seq));
+  const int qjl = a.S_v ? 1 : 0;
+  if (d == 64) {
+    hipLaunchKernelGGL(kv_merge_kernel<64>, grid, dim3(kKvMergeThreads), 0, s, a.partial, a.out, a.S_v,
+                       n_parts, a.group, qjl);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(kv_merge_kernel<128>, grid, dim3(kKvMergeThreads), 0, s, a.partial, a.out,
+                       a.S_v, n_parts, a.group, qjl);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
