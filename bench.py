@@ -244,11 +244,46 @@ def run_decode_step(api, torch, dev, cfg, p, q, K, V, codes, Vt, signs, perm, cb
             "call_ms": ms, "cache_tokens_per_s": n_seq * T / (ms * 1e-3)}
 
 
+def run_nano_latency(api, torch, dev, E, reps: int = 50):
+    """The NanoGPT-256 cache of one decode step (24 flattened layer-heads, 128
+    tokens, d64, fp32 keys and query): latency of the whole decode call, all
+    launches included; cache resident, no roofline claim."""
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS["nano_t128"]
+    inp = make_inputs(cfg)
+    n_seq, n_kv, T, d = inp["K"].shape
+    p = api.PgkqParams(d, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
+    K = torch.from_numpy(inp["K"]).to(dev)
+    Vt = api.pgkq_pack_values(torch.from_numpy(inp["V"]).to(dev), capacity=(T + 31) // 32 * 32)
+    q = torch.from_numpy(inp["q"]).to(dev)
+    signs = torch.from_numpy(inp["signs"]).to(dev)
+    S = torch.from_numpy(inp["S"]).to(dev)
+    _, _, cb = api.pgkq_calibrate(p, K)
+    codes = api.pgkq_encode(p, K, signs, None, cb, S, capacity=Vt.shape[2])
+    out = torch.empty((n_seq, cfg.n_q, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.pgkq_decode_workspace_bytes(p, n_seq, cfg.n_q, n_kv, T), dtype=torch.uint8, device=dev)
+    c0, c1 = E(), E()
+    ts = []
+    for r in range(reps + 5):
+        c0.record()
+        api.pgkq_decode_attn(p, q, codes, Vt, signs, None, cb, S, n_tokens=T, out=out, workspace=ws)
+        c1.record()
+        torch.cuda.synchronize()
+        if r >= 5:
+            ts.append(c0.elapsed_time(c1))
+    us = np.array(ts) * 1e3
+    return {"description": cfg.description, "latency_us_p50": float(np.median(us)),
+            "latency_us_p10": float(np.percentile(us, 10)), "latency_us_p90": float(np.percentile(us, 90)),
+            "note": "cache-resident, launch-bound: latency only"}
+
+
 def run_other_workloads(api, torch, dev, flush, E, reps: int = 20):
     """Decode of the other configurations of the pages' workload list on this
     GPU (NanoGPT-256 context with and without QJL, the 131k-token single
     stream): whole decode call and scan kernel, keys encoded and values packed
-    beforehand (inputs resident)."""
+    beforehand (inputs resident).  Cache tokens count every flattened layer.
+    The NanoGPT-256 context is also decoded from the fp16 cache (the FP16
+    comparator), with the fidelity of the PGKQ output against it."""
     from synth import CONFIGS, make_inputs
     res = {}
     for name in ("nano_b64_t512", "nano_b64_t512_b4", "gqa_b1_t131k"):
@@ -293,9 +328,40 @@ def run_other_workloads(api, torch, dev, flush, E, reps: int = 20):
         alg = n_seq * n_kv * T * (rb + 2 * d)
         res[name] = {"description": cfg.description, "record_bytes": rb,
                      "decode_call_ms": call_ms, "scan_ms": scan_ms,
-                     "cache_tokens_per_s": n_seq * T / (call_ms * 1e-3),
+                     "cache_tokens_per_s": n_seq * cfg.layers * T / (call_ms * 1e-3),
                      "scan_gbs": alg / (scan_ms * 1e-3) / 1e9,
                      "scan_frac": alg / (scan_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        if name == "nano_b64_t512":
+            # the FP16 comparator on the same keys (as fp16), values and queries
+            K16 = K.to(torch.float16)
+            out16 = torch.empty_like(out)
+            ws16 = torch.empty(max(api.pgkq_fp16_decode_workspace_bytes(d, n_seq, cfg.n_q, n_kv, T), 256),
+                               dtype=torch.uint8, device=dev)
+            f16 = []
+            for r in range(reps + 3):
+                flush.fill_(r & 255)
+                c0.record()
+                api.pgkq_fp16_decode_attn(q, K16, Vt, out=out16, workspace=ws16)
+                c1.record()
+                torch.cuda.synchronize()
+                if r >= 3:
+                    f16.append(c0.elapsed_time(c1))
+            f16_ms = float(np.median(f16))
+            api.pgkq_decode_attn(p, q, codes, Vt, signs, None, cb, S, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            a = out.double().flatten()
+            ref = out16.double().flatten()
+            res["nano_b64_t512_fp16"] = {
+                "description": "the same NanoGPT-256 context from the fp16 cache (FP16 comparator)",
+                "decode_call_ms": f16_ms,
+                "cache_tokens_per_s": n_seq * cfg.layers * T / (f16_ms * 1e-3),
+                "gbs": n_seq * n_kv * T * 4 * d / (f16_ms * 1e-3) / 1e9,
+                "pgkq_vs_fp16": {"max_abs": float((a - ref).abs().max()),
+                                 "rel_l2": float((a - ref).norm() / ref.norm()),
+                                 "cosine": float(torch.dot(a, ref) / (a.norm() * ref.norm())),
+                                 "note": "fidelity of the method on these synthetic inputs (the "
+                                         "float64 oracle gives the same figures), not a parity measure"}}
+            del K16, out16, ws16
         del K, Vt, q, codes, ws, inp
     return res
 
@@ -405,6 +471,7 @@ def main():
                                flush, E)
     controls = run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E)
     others = run_other_workloads(api, torch, dev, flush, E)
+    others["nano_t128_latency"] = run_nano_latency(api, torch, dev, E)
 
     token_heads = n_seq * n_kv * T
     alg_bytes = token_heads * (rb + 2 * d)

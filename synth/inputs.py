@@ -50,6 +50,7 @@ class WorkloadConfig:
     reorder: bool = False
     n_splits: int = 0
     description: str = ""
+    layers: int = 1  # model layers flattened into the kv-heads (cache tokens count each layer)
 
     @property
     def group(self) -> int:
@@ -73,12 +74,12 @@ CONFIGS = {
     # NanoGPT-256 cache, one decode step: 6 layers x 4 heads flattened into 24
     # kv-heads (= query heads), head_dim 64, 128 cached tokens.
     "nano_t128": WorkloadConfig("nano_t128", 1, 1, 24, 24, 128, 64, 3, 2, 64, "f32", "f32", 2, 8.0,
-                         description="NanoGPT-256 cache, 6Lx4H, d64, T128, B1, b3/2, QJL m64"),
+                         description="NanoGPT-256 cache, 6Lx4H, d64, T128, B1, b3/2, QJL m64", layers=6),
     # Full NanoGPT-256 context, batch 64.
     "nano_b64_t512": WorkloadConfig("nano_b64_t512", 2, 64, 24, 24, 512, 64, 3, 2, 64, "f32", "f32", 2, 8.0,
-                          description="NanoGPT-256 full context, B64, d64, T512, b3/2, QJL m64"),
+                          description="NanoGPT-256 full context, B64, d64, T512, b3/2, QJL m64", layers=6),
     "nano_b64_t512_b4": WorkloadConfig("nano_b64_t512_b4", 2, 64, 24, 24, 512, 64, 4, 3, 0, "f32", "f32", 2, 8.0,
-                          description="NanoGPT-256 full context, B64, d64, T512, b4/3, no QJL"),
+                          description="NanoGPT-256 full context, B64, d64, T512, b4/3, no QJL", layers=6),
     # GQA decode at scale.
     "gqa_b16_t32k": WorkloadConfig("gqa_b16_t32k", 3, 16, 32, 8, 32768, 128, 3, 2, 128, "f16", "bf16", 4, 10.0,
                          n_splits=8,
