@@ -46,7 +46,15 @@ struct ScanShape {
   static constexpr int A = 1 << BA;
   static constexpr int NCODES = 1 << P;
   static constexpr bool JOINT = N * NCODES * G <= 8192;  // <= 32 KiB of LDS
-  static constexpr int TABLE_FLOATS = JOINT ? N * NCODES * G : N * A * G + L;
+  // Floats per pair in the table: its block plus G floats of padding.  The
+  // table is written by one thread per (pair, head); unpadded, the pairs of a
+  // wavefront sit a multiple of 64 banks apart and every write is a 16-way
+  // bank conflict.  With the padding consecutive pairs start G banks apart, so
+  // the 64 / G pairs x G heads of a wavefront fill all 64 banks; the score's
+  // reads of G consecutive floats stay aligned.
+  static constexpr int PSTRIDE = (JOINT ? NCODES : A) * G + G;
+  static constexpr int TABLE_FLOATS = JOINT ? N * PSTRIDE : N * PSTRIDE + L;
+  static constexpr int QSTRIDE = 16 * G + G;  // floats per sketch nibble position, padded alike
 };
 
 template <int P>
@@ -211,7 +219,8 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   constexpr int M = QJL ? D : 0;
   constexpr int NC = N * P / 32;
   constexpr int NW = NC + M / 32;
-  constexpr int NQT = QJL ? (M / 4) * 16 * G : 1;
+  constexpr int PSTRIDE = SS::PSTRIDE, QSTRIDE = SS::QSTRIDE;
+  constexpr int NQT = QJL ? (M / 4) * QSTRIDE : 1;
   // table lookups per scheduling group: at most 32 table floats in flight (16
   // with coded values for 8 heads, whose accumulators take more registers)
   constexpr int PG_FLOATS = CODED_V && G >= 8 ? 16 : 32;
@@ -334,14 +343,14 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       if constexpr (JOINT) {
 #pragma unroll
         for (int code = 0; code < NCODES; ++code)
-          s_tab[(i * NCODES + code) * G + g] = lvr[code & (L - 1)] * lt[code >> BM];
+          s_tab[i * PSTRIDE + code * G + g] = lvr[code & (L - 1)] * lt[code >> BM];
       } else {
 #pragma unroll
-        for (int ac = 0; ac < A; ++ac) s_tab[(i * A + ac) * G + g] = lt[ac];
+        for (int ac = 0; ac < A; ++ac) s_tab[i * PSTRIDE + ac * G + g] = lt[ac];
       }
     }
     if constexpr (!JOINT) {
-      if (tid < L) s_tab[N * A * G + tid] = lvr[tid];
+      if (tid < L) s_tab[N * PSTRIDE + tid] = lvr[tid];
     }
   }
   if constexpr (CODED_V) {
@@ -366,7 +375,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       for (int nib = 0; nib < 16; ++nib) {
         const float v = ((nib & 1) ? q0 : -q0) + ((nib & 2) ? q1 : -q1) + ((nib & 4) ? q2 : -q2) +
                         ((nib & 8) ? q3 : -q3);
-        s_qt[(k * 16 + nib) * G + g] = kappa * v;
+        s_qt[k * QSTRIDE + nib * G + g] = kappa * v;
       }
     }
   }
@@ -394,12 +403,12 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       const uint32_t code = code_at<P>(cw, i);
       float e[G];
       if constexpr (JOINT) {
-        lds_fetch<G>(&s_tab[(i * NCODES + code) * G], e);
+        lds_fetch<G>(&s_tab[i * PSTRIDE + code * G], e);
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] += e[g];
       } else {
-        const float lvl = s_tab[N * A * G + (code & (L - 1))];
-        lds_fetch<G>(&s_tab[(i * A + (code >> BM)) * G], e);
+        const float lvl = s_tab[N * PSTRIDE + (code & (L - 1))];
+        lds_fetch<G>(&s_tab[i * PSTRIDE + (code >> BM) * G], e);
 #pragma unroll
         for (int g = 0; g < G; ++g) s[g] = fmaf(lvl, e[g], s[g]);
       }
@@ -417,7 +426,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
         }
         const uint32_t nib = (cw[NC + (k >> 3)] >> (4 * (k & 7))) & 15u;
         float e[G];
-        lds_fetch<G>(&s_qt[(k * 16 + nib) * G], e);
+        lds_fetch<G>(&s_qt[k * QSTRIDE + nib * G], e);
 #pragma unroll
         for (int g = 0; g < G; ++g) qs[g] += e[g];
       }
