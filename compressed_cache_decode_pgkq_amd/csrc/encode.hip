@@ -94,8 +94,7 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
   const int64_t b = blockIdx.z;
 
   __shared__ double s_T2[L];
-  __shared__ double s_LC[L * A];
-  __shared__ double s_LS[L * A];
+  __shared__ double2 s_LCS[L * A];  // level * (cos, sin) of each joint code: one 16-byte read
   __shared__ int s_inv[D];
   __shared__ __align__(16) unsigned char s_key[kTile * RST];
   __shared__ __align__(16) _Float16 s_E[2 * kTile * EST];
@@ -119,8 +118,7 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
     double sn, cs;
     sincospi(-1.0 + (2.0 * ac + 1.0) / double(A), &sn, &cs);
     const double lv = double(cb[rc]);
-    s_LC[e] = lv * cs;
-    s_LS[e] = lv * sn;
+    s_LCS[e] = make_double2(lv * cs, lv * sn);
   }
   // inverse of the channel order: input channel c' lands at position s_inv[c']
   for (int p = tid; p < D; p += kThreads) s_inv[a.perm ? int(a.perm[size_t(h) * D + p]) : p] = p;
@@ -287,8 +285,9 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
       if ((p & 3) == 0) cpack[p >> 2] = code;
       else cpack[p >> 2] |= code << (8 * (p & 3));
       if constexpr (QJL) {
-        const double ex = xx * inv_scale - s_LC[rc * A + ac];
-        const double ey = yy * inv_scale - s_LS[rc * A + ac];
+        const double2 lcs = s_LCS[rc * A + ac];
+        const double ex = xx * inv_scale - lcs.x;
+        const double ey = yy * inv_scale - lcs.y;
         x[2 * p] = ex;
         x[2 * p + 1] = ey;
         ss += ex * ex + ey * ey;
