@@ -58,6 +58,17 @@ __device__ __forceinline__ void split_f16(double x, _Float16& hi, _Float16& lo) 
   lo = static_cast<_Float16>(xf - static_cast<float>(hi));
 }
 
+// split_f16(x 2^e): the power-of-two scale applied after the fp32 rounding
+// (an exponent add at fp32 rate instead of a float64 product).  Equal unless
+// x 2^e is below the fp32 normal range, where both give fp16 parts of 0.
+__device__ __forceinline__ void split_f16_scaled(double x, int e, _Float16& hi, _Float16& lo) {
+  float xf = static_cast<float>(x);
+  pin_reg(xf);
+  xf = ldexpf(xf, e);
+  hi = static_cast<_Float16>(xf);
+  lo = static_cast<_Float16>(xf - static_cast<float>(hi));
+}
+
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
   return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
 }
@@ -312,14 +323,14 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
       // to [1, 2): exact, and no sign changes
       double m1 = fmax(mx, quad_xor<1>(mx));
       m1 = fmax(m1, quad_xor<2>(m1));
-      const double scl = m1 > 0.0 ? ldexp(1.0, -ilogb(m1)) : 1.0;
+      const int sexp = m1 > 0.0 ? -ilogb(m1) : 0;
       _Float16* Ehi = s_E + j * EST + qt * CPT;
       _Float16* Elo = s_E + kTile * EST + j * EST + qt * CPT;
 #pragma unroll
       for (int v = 0; v < CPT / 8; ++v) {
         _Float16 hi[8], lo[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) split_f16(x[8 * v + e] * scl, hi[e], lo[e]);
+        for (int e = 0; e < 8; ++e) split_f16_scaled(x[8 * v + e], sexp, hi[e], lo[e]);
         *reinterpret_cast<u32x4*>(Ehi + 8 * v) =
             u32x4{pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7])};
         *reinterpret_cast<u32x4*>(Elo + 8 * v) =
