@@ -21,7 +21,10 @@
 // transposed through a wave-private LDS block.  The wavefronts' states
 // (m, l, o[d], a[m]) are merged in the workgroup into one partial per split.
 // A lane holds G CPL pair accumulators: CPL = 8 up to 4 query heads, 4 for 8
-// heads (twice the rows per lane, half the registers).
+// heads (twice the rows per lane, half the registers).  With 8 heads the
+// sketch sums stay on the vector ALU (lane = CPL sketch bits of a row: a_j
+// accumulated directly): the matrix-core operands would push the registers and
+// LDS of the workgroup past the limits of two workgroups per compute unit.
 #pragma once
 
 #include "mfma_pv.hpp"
@@ -40,12 +43,14 @@ struct CodedPV {
   static constexpr int CPL = G >= 8 ? 4 : 8;    // channels per lane
   static constexpr int PPL = CPL / 2;           // pairs per lane
   static constexpr int LPT = D / CPL;           // lanes per token row
+  static constexpr bool SKM = QJLV && G <= 4;    // sketch sums on the matrix cores
+  static constexpr bool SKV = QJLV && !SKM;      // sketch sums on the vector ALU
   static constexpr int NSWV = M / 32;           // sketch words per token
-  static constexpr int NB = QJLV ? M / 16 : 1;  // 16-column blocks of the sketch
+  static constexpr int NB = SKM ? M / 16 : 1;   // 16-column blocks of the sketch
   static constexpr int KS = kWave / 32;         // 32-token steps per chunk
   static constexpr float kPScale = 32768.f;     // 2^15: keeps hi in the normal fp16 range
   // LDS bytes of one wavefront's sketch weight rows ([hi, lo][G][64] fp16)
-  static constexpr int P16_BYTES = QJLV ? 2 * G * kWave * 2 : 16;
+  static constexpr int P16_BYTES = SKM ? 2 * G * kWave * 2 : 16;
   static constexpr int TPI = kWave / LPT;      // rows per pass
   static constexpr int NIT = kWave / TPI;      // passes per chunk
   static constexpr int WIDTH = 2 * D + 4;      // partial row: m, l, -, -, o[D], a[D]
@@ -58,7 +63,8 @@ struct CodedPV {
   static_assert(LPT <= kWave, "lanes per token row");
 
   float m_run[G], l_lane[G], o[G][CPL], spn[G];
-  f32x4 sacc[NB];  // c of the sketch, C layout of the matrix product (scaled by 2^15)
+  f32x4 sacc[NB];                            // c, C layout of the matrix product (scaled by 2^15)
+  float acc[SKV ? G : 1][SKV ? CPL : 1];     // sum_t p_t nu_t bit_tj of this lane's bits
   int lane, wave, slot, dblk;
   uint32_t row_bytes, nu_off;
 
@@ -84,6 +90,10 @@ struct CodedPV {
     }
 #pragma unroll
     for (int n = 0; n < NB; ++n) sacc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < (SKV ? G : 1); ++g)
+#pragma unroll
+      for (int k = 0; k < (SKV ? CPL : 1); ++k) acc[g][k] = 0.f;
   }
 
   // code words of token c0 + lane (the whole stream is the buffer range;
@@ -117,12 +127,16 @@ struct CodedPV {
         spn[g] *= alpha[g];
 #pragma unroll
         for (int k = 0; k < CPL; ++k) o[g][k] *= alpha[g];
+        if constexpr (SKV) {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) acc[g][k] *= alpha[g];
+        }
         m_run[g] = mnew;
         grew = true;
       }
       pv[g] = valid ? fast_exp2(z - m_run[g]) : 0.f;
       l_lane[g] += pv[g];
-      if constexpr (QJLV) {
+      if constexpr (SKM) {
         if (valid) spn[g] = fmaf(pv[g], nu_t, spn[g]);
         const float ps = pv[g] * kPScale;
         const _Float16 hi = static_cast<_Float16>(ps);
@@ -131,7 +145,7 @@ struct CodedPV {
         p16[(G + g) * kWave + lane] = lo;
       }
     }
-    if constexpr (QJLV) {
+    if constexpr (SKM) {
       if (grew) {  // wave-uniform: rescale the sketch rows of the heads whose maximum grew
         // lane l holds rows 4(l/16) + r of every block
         float f[4];
@@ -160,7 +174,8 @@ struct CodedPV {
     }
 #pragma unroll
     for (int w = 0; w < NW; ++w) vw[w * VW_STRIDE + lane] = vc.w[w];
-    if constexpr (QJLV) vw[NW * VW_STRIDE + lane] = (c0 + lane < c_end) ? (vc.nu & 0xFFFFu) : 0u;
+    if constexpr (SKM) vw[NW * VW_STRIDE + lane] = (c0 + lane < c_end) ? (vc.nu & 0xFFFFu) : 0u;
+    if constexpr (SKV) vw[NW * VW_STRIDE + lane] = vc.nu;
     wave_lds_sync();
 
     const int o0 = PPL * P * dblk;  // first polar bit of this lane's pairs
@@ -184,8 +199,25 @@ struct CodedPV {
           o[g][2 * j + 1] = fmaf(pp[g], t.y, o[g][2 * j + 1]);
         }
       }
+      if constexpr (SKV) {
+        constexpr uint32_t smask = (1u << CPL) - 1u;
+        const uint32_t sb =
+            (vw[(NC + (CPL * dblk) / 32) * VW_STRIDE + r] >> ((CPL * dblk) & 31)) & smask;
+        const float nu = half_bits_to_float(static_cast<uint16_t>(vw[NW * VW_STRIDE + r]));
+        const bool live = c0 + r < c_end;  // a slot past the cache may hold any bits
+        float fb[CPL];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) fb[k] = static_cast<float>((sb >> k) & 1u);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float pn = live ? pp[g] * nu : 0.f;
+          spn[g] += pn;
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) acc[g][k] = fmaf(fb[k], pn, acc[g][k]);
+        }
+      }
     }
-    if constexpr (QJLV) {
+    if constexpr (SKM) {
       // c += P (bit * nu): lane l supplies A[head l % 16][tokens 8 (l / 16) ..]
       // and B[tokens 8 (l / 16) + j][sketch column 16 n + l % 16]; a token
       // past c_end has nu = 0 in the block, so its bits do not matter
@@ -230,9 +262,15 @@ struct CodedPV {
 #pragma unroll
     for (int off = LPT; off < kWave; off <<= 1) {
 #pragma unroll
-      for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int k = 0; k < CPL; ++k) o[g][k] += __shfl_xor(o[g][k], off, kWave);
+        if constexpr (SKV) {
+          spn[g] += __shfl_xor(spn[g], off, kWave);
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) acc[g][k] += __shfl_xor(acc[g][k], off, kWave);
+        }
+      }
     }
   }
 
@@ -248,7 +286,7 @@ struct CodedPV {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       l_w[g] = wave_sum(l_lane[g]);
-      s_w[g] = QJLV ? wave_sum(spn[g]) : 0.f;
+      s_w[g] = SKM ? wave_sum(spn[g]) : 0.f;  // (with SKV every lane group holds the wave's sum)
     }
     float* wm = scratch;                  // [WAVES][G]
     float* wl = scratch + WAVES * G;      // [WAVES][G]
@@ -257,16 +295,22 @@ struct CodedPV {
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) wo[(wave * G + g) * 2 * D + dblk * CPL + k] = o[g][k];
+        for (int k = 0; k < CPL; ++k) {
+          wo[(wave * G + g) * 2 * D + dblk * CPL + k] = o[g][k];
+          if constexpr (!SKM)
+            wo[(wave * G + g) * 2 * D + D + dblk * CPL + k] = SKV ? 2.f * acc[g][k] - spn[g] : 0.f;
+        }
     }
-    // a = 2 c - s; lane l holds c of head 4 (l / 16) + r, column 16 n + l % 16
+    if constexpr (SKM) {
+      // a = 2 c - s; lane l holds c of head 4 (l / 16) + r, column 16 n + l % 16
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if ((lane >> 4) == (g >> 2)) {
+      for (int g = 0; g < G; ++g) {
+        if ((lane >> 4) == (g >> 2)) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n)
-          wo[(wave * G + g) * 2 * D + D + 16 * n + (lane & 15)] =
-              QJLV ? 2.f * (sacc[n][g & 3] * (1.f / kPScale)) - s_w[g] : 0.f;
+          for (int n = 0; n < NB; ++n)
+            wo[(wave * G + g) * 2 * D + D + 16 * n + (lane & 15)] =
+                2.f * (sacc[n][g & 3] * (1.f / kPScale)) - s_w[g];
+        }
       }
     }
     if (lane == 0) {

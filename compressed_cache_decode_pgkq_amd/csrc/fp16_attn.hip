@@ -52,10 +52,11 @@ __device__ __forceinline__ int keep_bits(int k) {
   return (k0 ^ k2) | ((k1 ^ k2) << 1) | (k2 << 2) | (k3 << 3);
 }
 
-// 8 query heads at d = 128 hold 64 query and 64 accumulator registers per lane:
-// one wavefront per SIMD, so that the register file (and AGPRs) has room.
+// Two wavefronts per SIMD for every shape: with 8 query heads at d = 128 (64
+// query and 64 accumulator registers per lane) the 256-register budget still
+// holds them without spilling, and the second wavefront hides the key loads.
 template <int D, int G>
-constexpr int fp16_min_waves() { return G * D > 512 ? 1 : 2; }
+constexpr int fp16_min_waves() { return 2; }
 
 template <int D, int G, bool WAVE_PARTS>
 __global__ void __launch_bounds__(kThreads, (fp16_min_waves<D, G>()))
