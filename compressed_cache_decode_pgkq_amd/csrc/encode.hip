@@ -58,15 +58,23 @@ __device__ __forceinline__ void split_f16(double x, _Float16& hi, _Float16& lo) 
   lo = static_cast<_Float16>(xf - static_cast<float>(hi));
 }
 
-// split_f16(x 2^e): the power-of-two scale applied after the fp32 rounding
-// (an exponent add at fp32 rate instead of a float64 product).  Equal unless
-// x 2^e is below the fp32 normal range, where both give fp16 parts of 0.
-__device__ __forceinline__ void split_f16_scaled(double x, int e, _Float16& hi, _Float16& lo) {
-  float xf = static_cast<float>(x);
-  pin_reg(xf);
-  xf = ldexpf(xf, e);
-  hi = static_cast<_Float16>(xf);
-  lo = static_cast<_Float16>(xf - static_cast<float>(hi));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// split_f16 of x0 2^e and x1 2^e, returned as packed fp16 pairs.  The
+// power-of-two scale is applied after the fp32 rounding (an exponent add at
+// fp32 rate instead of a float64 product; equal unless x 2^e is below the fp32
+// normal range, where both give fp16 parts of 0); the round-to-nearest-even
+// conversions to fp16 take two elements per instruction.
+__device__ __forceinline__ void split2_f16_scaled(double x0, double x1, int e, uint32_t& hi2, uint32_t& lo2) {
+  float f0 = static_cast<float>(x0), f1 = static_cast<float>(x1);
+  pin_reg(f0);
+  pin_reg(f1);
+  const f32x2 xf = {ldexpf(f0, e), ldexpf(f1, e)};
+  const f16x2 h = __builtin_convertvector(xf, f16x2);
+  const f32x2 l = xf - __builtin_convertvector(h, f32x2);  // exact
+  hi2 = __builtin_bit_cast(uint32_t, h);
+  lo2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(l, f16x2));
 }
 
 __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
@@ -328,13 +336,11 @@ encode_kernel(EncodeArgs a, const float* __restrict__ S, const uint8_t* __restri
       _Float16* Elo = s_E + kTile * EST + j * EST + qt * CPT;
 #pragma unroll
       for (int v = 0; v < CPT / 8; ++v) {
-        _Float16 hi[8], lo[8];
+        uint32_t hq[4], lq[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) split_f16_scaled(x[8 * v + e], sexp, hi[e], lo[e]);
-        *reinterpret_cast<u32x4*>(Ehi + 8 * v) =
-            u32x4{pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7])};
-        *reinterpret_cast<u32x4*>(Elo + 8 * v) =
-            u32x4{pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7])};
+        for (int e = 0; e < 4; ++e) split2_f16_scaled(x[8 * v + 2 * e], x[8 * v + 2 * e + 1], sexp, hq[e], lq[e]);
+        *reinterpret_cast<u32x4*>(Ehi + 8 * v) = u32x4{hq[0], hq[1], hq[2], hq[3]};
+        *reinterpret_cast<u32x4*>(Elo + 8 * v) = u32x4{lq[0], lq[1], lq[2], lq[3]};
       }
     }
     __syncthreads();
