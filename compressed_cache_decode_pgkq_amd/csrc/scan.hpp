@@ -384,7 +384,13 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   for (int64_t c0 = c_first; c0 < c_end; c0 += c_step) {
     const int64_t t = c0 + lane;
     const bool valid = t < c_end;
-    if (!EARLY || c0 != c_first) issue(c0);
+    if (!EARLY || c0 != c_first) {
+      // a wavefront requesting its chunk goes ahead of the ones computing:
+      // the loads are in flight sooner (131k-token stream 68-70 -> 66 us)
+      __builtin_amdgcn_s_setprio(2);
+      issue(c0);
+      __builtin_amdgcn_s_setprio(0);
+    }
 
     float s[G];
 #pragma unroll
