@@ -6,15 +6,19 @@ a serving loop can capture a decode call into a graph and replay it.  Each
 case captures one call, then replays the graph several times with eager work
 and synchronizations in between; every replay must equal the eager call on
 the same inputs bit for bit, also after a query was overwritten in place
-(the graph reads the current contents of its buffers).
+(the graph reads the current contents of its buffers).  Covered: the PGKQ
+decode (split and single-workgroup launches), the fused append + decode step,
+the PGKQ-KV decode and the FP16-cache comparator.
 """
 
+import numpy as np
 import pytest
 import torch
 
 from synth import CONFIGS
 
-from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev
+from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev, v_cache, value_capacity
+from parity_util import codebook_array
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +114,69 @@ def test_decode_step_replays_in_a_graph():
     def call(out):
         api.pgkq_decode_step(p, q, k_new, v_new, codes, dev["V"], T, dev["signs"], dev["perm"],
                              dev["codebook"], dev["S"], out=out, workspace=ws)
+
+    call(out_e)
+    torch.cuda.synchronize()
+    g = _capture(lambda: call(out_g))
+    _replays_match(g, out_g, out_e)
+
+
+@pytest.mark.parametrize("n_q,n_splits", [(32, 3), (64, 3), (32, 0)])
+def test_kv_decode_replays_in_a_graph(n_q, n_splits):
+    """PGKQ-KV (values coded too): 4 query heads per kv-head (sketch sums on
+    the matrix cores) and 8 (sketch sums on the vector ALU)."""
+    from test_gpu_kv import KVCase
+    api = _api()
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=700, n_q=n_q)
+    case = KVCase(cfg, 3)
+    k = case.k
+    dev = k.dev_inputs()
+    ck = to_dev(k.oracle_codes())
+    cv = to_dev(case.oracle_v_codes())
+    pk, pv = lib_params(k.p), lib_params(case.pv)
+    q = q_tensor(k.q, cfg.q_dtype)
+    n_seq, _, d = q.shape
+    cbv = to_dev(codebook_array(case.v_tables))
+    Sv = to_dev(case.Sv)
+    ws = torch.empty(api.pgkq_kv_decode_workspace_bytes(pk, pv, n_seq, n_q, cfg.n_kv, k.T, n_splits),
+                     dtype=torch.uint8, device=q.device)
+    out_e = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    out_g = torch.empty_like(out_e)
+
+    def call(out):
+        api.pgkq_kv_decode_attn(pk, pv, q, ck, cv, cfg.n_kv, k.cap, dev["signs"], dev["perm"],
+                                dev["codebook"], dev["S"], cbv, Sv, n_tokens=k.T, n_splits=n_splits,
+                                out=out, workspace=ws)
+
+    call(out_e)
+    torch.cuda.synchronize()
+    g = _capture(lambda: call(out_g))
+    _replays_match(g, out_g, out_e)
+
+
+@pytest.mark.parametrize("n_splits", [3, 0])
+def test_fp16_decode_replays_in_a_graph(n_splits):
+    """The FP16-cache comparator."""
+    from synth import make_inputs
+    api = _api()
+    cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_tokens=700)
+    inp = make_inputs(cfg)
+    T = cfg.n_tokens
+    cap = value_capacity(T)
+    n_seq, n_kv, d = cfg.n_seq, cfg.n_kv, cfg.head_dim
+    Kp = np.zeros((n_seq, n_kv, cap, d), np.float16)
+    Kp[:, :, :T] = inp["K"][:, :, :T].astype(np.float16)
+    K16 = to_dev(Kp)
+    V16 = v_cache(inp["V"][:, :, :T], cap)
+    q = q_tensor(inp["q"], cfg.q_dtype)
+    n_q = q.shape[1]
+    ws = torch.empty(api.pgkq_fp16_decode_workspace_bytes(d, n_seq, n_q, n_kv, T, n_splits),
+                     dtype=torch.uint8, device=q.device)
+    out_e = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    out_g = torch.empty_like(out_e)
+
+    def call(out):
+        api.pgkq_fp16_decode_attn(q, K16, V16, n_tokens=T, n_splits=n_splits, out=out, workspace=ws)
 
     call(out_e)
     torch.cuda.synchronize()
