@@ -539,6 +539,8 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   a.scale_log2 = scale * 1.4426950408889634f;
   a.append_slot = -1;
   if (step) {
+    // the preparation launch holds n_q + n_kv grid rows
+    if (n_q + n_kv > kMaxGridYZ) return PGKQ_ERR_SHAPE;
     a.append_slot = step->slot;
     a.k_new = step->k_new;
     a.k_dtype = static_cast<int>(step->k_dtype);

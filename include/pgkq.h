@@ -208,8 +208,9 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
  * n_cached + 1.  The append runs inside the query-preparation launch (no
  * extra kernel); its decisions are taken in float64 on the unnormalized
  * transform and its QJL projection is accumulated in float64.  Requires
- * 0 <= n_cached < capacity; workspace as pgkq_decode_workspace_bytes() for
- * n_cached + 1 tokens.  codes and V are written (slot n_cached only). */
+ * 0 <= n_cached < capacity and n_q + n_kv <= 65535 (else PGKQ_ERR_SHAPE);
+ * workspace as pgkq_decode_workspace_bytes() for n_cached + 1 tokens.  codes
+ * and V are written (slot n_cached only). */
 pgkq_status pgkq_decode_step(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
                              const void* k_new, pgkq_dtype k_dtype, const void* v_new,
                              int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_cached,

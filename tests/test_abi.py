@@ -352,6 +352,22 @@ def test_value_cache_capacity_must_be_a_tile_multiple():
     assert st == L.PGKQ_ERR_SHAPE
 
 
+def test_decode_step_grid_rows_limit():
+    """The preparation launch of a step holds n_q + n_kv grid rows: at most
+    65535.  With 8 query heads per kv-head n_kv = 7282 gives 65538 rows and
+    is rejected before anything is enqueued (n_q = 58256 alone is within the
+    limit of a plain decode)."""
+    o = L.PgkqLaunchOpts(0, None, None)
+
+    def call(n_kv):
+        return L.lib().pgkq_decode_step(_params(128, 3, 2, 128, 1), _vp(A), L.PGKQ_BF16, _vp(A),
+                                        L.PGKQ_F16, _vp(A), 1, 8 * n_kv, n_kv, 99, 128, _vp(A), None,
+                                        _vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 0.0, ctypes.byref(o),
+                                        _vp(A), 1 << 40, None)
+
+    assert call(7282) == L.PGKQ_ERR_SHAPE
+
+
 def test_pack_values_validation():
     lib = L.lib()
 
