@@ -255,6 +255,118 @@ def test_p4_scaled_table_is_fp32_rounding_of_product():
     assert np.array_equal(lv2, lv) and np.array_equal(th2, th)
 
 
+# ------------------------------------------------------- radius unit of the per-head table
+# The table is built in rho units, rho = (r / ||k||) sqrt(d/2), and scaled into
+# radius units by the head scale.  For keys of one fixed norm c the calibrated
+# head scale is c, so the radius of a pair after the transform, r = rho c /
+# sqrt(d/2), follows the Beta-prior law in those units exactly.  The checks
+# below draw such keys, take the table the oracle builds for them
+# (channel_sumsq -> head_scale -> scaled_table) and test physical statements
+# about the sampled radii: the mass below every threshold, the centroid of every
+# cell, and a KS test of the radii against the law implied by the table.
+
+
+def _fixed_norm_radii(d, n_keys, seed, norm=3.7):
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((n_keys, d))
+    K = norm * g / np.linalg.norm(g, axis=1, keepdims=True)
+    signs = rng.choice([-1, 1], size=d)
+    kt = rht.forward(K, signs)
+    # one pair per key (the pair index cycles), so the radii are independent
+    i = np.arange(n_keys) % (d // 2)
+    r = np.hypot(kt[np.arange(n_keys), 2 * i], kt[np.arange(n_keys), 2 * i + 1])
+    return K, r
+
+
+def _table_fits_radii(levels32, thresholds32, c, t, r, n):
+    """(ok, details): the absolute table agrees with the sampled radii under the
+    Beta-prior law within 5 standard errors at every threshold and cell, and the
+    radii pass a KS test against the law in the table's own unit."""
+    lv = np.asarray(levels32, dtype=np.float64)
+    th = np.asarray(thresholds32, dtype=np.float64)
+    N = r.size
+    fails = []
+    for j in range(len(th)):
+        p = float(codebook.rho_cdf(t[j], n))
+        frac = float(np.mean(r <= th[j]))
+        se = math.sqrt(p * (1 - p) / N)
+        if abs(frac - p) > 5 * se:
+            fails.append(("mass", j, frac, p))
+    cell = np.searchsorted(th, r, side="left")  # #{T_j < r}
+    for j in range(len(lv)):
+        rr = r[cell == j]
+        if rr.size < 100:
+            fails.append(("empty", j, rr.size))
+            continue
+        se = rr.std() / math.sqrt(rr.size)
+        if abs(rr.mean() - lv[j]) > 5 * se:
+            fails.append(("centroid", j, rr.mean(), lv[j], se))
+    unit = lv[-1] / c[-1]
+    ks = stats.kstest(r / unit, lambda x: codebook.rho_cdf(x, n))
+    if ks.pvalue <= 1e-3:
+        fails.append(("ks", ks.pvalue))
+    return not fails, fails
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_radius_unit_of_scaled_table_matches_the_prior(d):
+    n = d // 2
+    K, r = _fixed_norm_radii(d, 200_000, seed=1000 + d)
+    c, t = codebook.lloyd_max_beta(d, 3)
+    s_h = calibrate.head_scale(calibrate.channel_sumsq(K), K.shape[0])
+    assert abs(s_h - 3.7) < 1e-12
+    lv, th = codebook.scaled_table(c, t, s_h, d)
+    ok, why = _table_fits_radii(lv, th, c, t, r, n)
+    assert ok, why
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_radius_unit_check_rejects_other_scalings(d):
+    """The check above has the power to catch a wrong radius unit: s_h / sqrt(d)
+    and s_h sqrt(d/2) in place of s_h / sqrt(d/2) both fail it."""
+    n = d // 2
+    K, r = _fixed_norm_radii(d, 200_000, seed=2000 + d)
+    c, t = codebook.lloyd_max_beta(d, 3)
+    s_h = calibrate.head_scale(calibrate.channel_sumsq(K), K.shape[0])
+    # scaled_table divides by sqrt(d/2); feed it the head scale that yields the wrong unit
+    for wrong in (s_h / math.sqrt(2.0), s_h * n):
+        lv, th = codebook.scaled_table(c, t, wrong, d)
+        ok, _ = _table_fits_radii(lv, th, c, t, r, n)
+        assert not ok
+
+
+def test_gqa_head_mapping_of_decode_cache_by_hand():
+    """8 query heads over 2 kv-heads: heads 0-3 read kv-head 0 and heads 4-7 read
+    kv-head 1 (query 3 -> kv 0, query 4 -> kv 1), each checked against attention
+    computed explicitly on that kv-head's dequantized keys."""
+    rng = np.random.default_rng(77)
+    d, T = 16, 30
+    p = Params(d, 3, 2, d)
+    kv_of = [0, 0, 0, 0, 1, 1, 1, 1]
+    K = rng.standard_normal((1, 2, T, d)) * np.array([1.0, 3.0])[None, :, None, None]
+    V = rng.standard_normal((1, 2, T, d)) + np.array([-5.0, 5.0])[None, :, None, None]
+    q = rng.standard_normal((1, 8, d))
+    signs = rng.choice([-1, 1], size=(2, d))
+    S = rng.standard_normal((2, d, d)).astype(np.float32)
+    c, t = codebook.lloyd_max_beta(d, 3)
+    tables = []
+    for h in range(2):
+        ss = calibrate.channel_sumsq(K[0, h])
+        tables.append(codebook.scaled_table(c, t, calibrate.head_scale(ss, T), d))
+    fields = encode.encode_cache(K, signs, None, tables, S, p)
+    out, lg = attn.decode_cache(q, fields, V, tables, S, signs, None, p)
+    for hq in range(8):
+        h = kv_of[hq]
+        Khat = attn.dequantize_keys(fields[0][h], tables[h][0], S[h], signs[h], None, p)
+        s = Khat @ q[0, hq]
+        w = np.exp((s - s.max()) / math.sqrt(d))
+        ref = (w / w.sum()) @ V[0, h]
+        np.testing.assert_allclose(lg[0, hq], s, rtol=1e-11, atol=1e-11)
+        np.testing.assert_allclose(out[0, hq], ref, rtol=1e-11, atol=1e-11)
+    # the value means of the two kv-heads differ by 10: a wrong mapping cannot pass
+    assert np.all(out[0, :4].mean(axis=1) < -2) and np.all(out[0, 4:].mean(axis=1) > 2)
+
+
 # ------------------------------------------------------------ calibrate (step 0)
 
 def test_reorder_hand_examples():
