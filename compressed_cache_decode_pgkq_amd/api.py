@@ -56,6 +56,46 @@ def _half(t):
     return _ptr(t)
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _expect_shape(t, shape, what):
+    """Raise before anything is launched when a tensor's shape is not the one the
+    call's sizes imply (the C ABI sees pointers only, so this check lives here)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _expect_codes(codes, n_streams, capacity, record, what="codes"):
+    if record == 0:
+        return  # invalid parameters: the library call itself reports them
+    want = int(n_streams) * int(capacity) * int(record)
+    got = _nbytes(codes)
+    if got != want:
+        raise ValueError(f"{what}: {got} bytes, expected n_seq * n_kv * capacity * record bytes "
+                         f"= {n_streams} * {capacity} * {record} = {want}")
+
+
+def _code_capacity(codes, n_streams, record, what="codes"):
+    """Slots per stream of an existing code buffer (its size must be a whole number of them)."""
+    per = int(n_streams) * int(record)
+    if per <= 0:
+        return 1  # invalid parameters: the library call itself reports them
+    got = _nbytes(codes)
+    if got % per:
+        raise ValueError(f"{what}: {got} bytes is not a whole number of "
+                         f"n_seq * n_kv * record = {per}-byte slot rows")
+    return got // per
+
+
+def default_capacity(n_tokens: int) -> int:
+    """Slots per stream used when the caller gives none: n_tokens rounded up to the
+    32-token value tile (the same rule as pgkq_pack_values), so that the key codes
+    and the value cache of one stream always agree."""
+    return max(32, (int(n_tokens) + 31) // 32 * 32)
+
+
 def _stream(stream):
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
@@ -129,13 +169,21 @@ def pgkq_calibrate(params: PgkqParams, K: torch.Tensor, reorder: bool = False, s
 
 def pgkq_encode(params: PgkqParams, K: torch.Tensor, signs: torch.Tensor, perm, codebook,
                 S, codes=None, capacity=None, token_offset: int = 0, stream=None):
-    """Encode K [n_seq, n_kv, n_tokens, d] into codes [n_seq, n_kv, capacity * record] uint8."""
+    """Encode K [n_seq, n_kv, n_tokens, d] into codes [n_seq, n_kv, capacity * record] uint8.
+
+    Without ``codes`` a zeroed buffer of ``capacity`` slots per stream is made
+    (default: n_tokens rounded up to 32, as for the value cache); with ``codes``
+    its size must be n_seq * n_kv * capacity * record bytes (capacity defaults to
+    what the buffer holds)."""
     n_seq, n_kv, n_tok, d = K.shape
-    cap = int(capacity) if capacity is not None else n_tok
     p = params.c()
+    rb = pgkq_record_bytes(params)
     if codes is None:
-        rb = pgkq_record_bytes(params)
+        cap = int(capacity) if capacity is not None else default_capacity(n_tok)
         codes = torch.zeros((n_seq, n_kv, cap * rb), dtype=torch.uint8, device=K.device)
+    else:
+        cap = int(capacity) if capacity is not None else _code_capacity(codes, n_seq * n_kv, rb)
+        _expect_codes(codes, n_seq * n_kv, cap, rb)
     st = L.lib().pgkq_encode(ctypes.byref(p), _ptr(K), _dtype(K), n_seq, n_kv, n_tok, _ptr(signs),
                              _ptr(perm), _ptr(codebook), _ptr(S), _ptr(codes), cap,
                              int(token_offset), _stream(stream))
@@ -156,11 +204,14 @@ def pgkq_decode_attn(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, V
     [n_seq, n_kv, cap, d] in 32-token tiles (pgkq_pack_values)."""
     n_seq, n_q, d = q.shape
     n_kv, cap = V.shape[1], V.shape[2]
+    _expect_shape(V, (n_seq, n_kv, cap, d), "V")
+    _expect_codes(codes, n_seq * n_kv, cap, pgkq_record_bytes(params))
     n_tok = cap if n_tokens is None else int(n_tokens)
     p = params.c()
     o = _opts(n_splits, events)
     if out is None:
         out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    _expect_shape(out, (n_seq, n_q, d), "out")
     nb = int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(p), n_seq, n_q, n_kv, n_tok,
                                                   ctypes.byref(o)))
     ws, wsb = _ws(nb, q.device, workspace)
@@ -180,10 +231,15 @@ def pgkq_decode_step(params: PgkqParams, q: torch.Tensor, k_new: torch.Tensor,
     then decode attention over n_cached + 1 tokens -> out [n_seq, n_q, d]."""
     n_seq, n_q, d = q.shape
     n_kv, cap = V.shape[1], V.shape[2]
+    _expect_shape(V, (n_seq, n_kv, cap, d), "V")
+    _expect_shape(k_new, (n_seq, n_kv, d), "k_new")
+    _expect_shape(v_new, (n_seq, n_kv, d), "v_new")
+    _expect_codes(codes, n_seq * n_kv, cap, pgkq_record_bytes(params))
     p = params.c()
     o = _opts(n_splits, events)
     if out is None:
         out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    _expect_shape(out, (n_seq, n_q, d), "out")
     nb = int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(p), n_seq, n_q, n_kv,
                                                   int(n_cached) + 1, ctypes.byref(o)))
     ws, wsb = _ws(nb, q.device, workspace)
@@ -201,10 +257,12 @@ def pgkq_estimate_logits(params: PgkqParams, q: torch.Tensor, codes: torch.Tenso
                          workspace=None, stream=None):
     """Raw logits [n_seq, n_q, n_tokens] fp32 (no softmax scale)."""
     n_seq, n_q, d = q.shape
+    _expect_codes(codes, n_seq * n_kv, capacity, pgkq_record_bytes(params))
     n_tok = capacity if n_tokens is None else int(n_tokens)
     p = params.c()
     if logits is None:
         logits = torch.empty((n_seq, n_q, n_tok), dtype=torch.float32, device=q.device)
+    _expect_shape(logits, (n_seq, n_q, n_tok), "logits")
     nb = int(L.lib().pgkq_decode_workspace_bytes(ctypes.byref(p), n_seq, n_q, n_kv, n_tok, None))
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_estimate_logits(ctypes.byref(p), _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok,
@@ -236,9 +294,10 @@ def pgkq_pack_values(rows: torch.Tensor, capacity=None, cache=None, slot_offset:
     rounded up to 32)."""
     n_seq, n_kv, T, d = rows.shape
     if cache is None:
-        cap = int(capacity) if capacity is not None else max(32, (T + 31) // 32 * 32)
+        cap = int(capacity) if capacity is not None else default_capacity(T)
         cache = torch.zeros((n_seq, n_kv, cap, d), dtype=torch.float16, device=rows.device)
     cap = cache.shape[2]
+    _expect_shape(cache, (n_seq, n_kv, cap, d), "cache")
     rows = rows.contiguous()
     st = L.lib().pgkq_pack_values(_half(rows), n_seq * n_kv, T, d, _half(cache), cap, int(slot_offset),
                                   _stream(stream))
@@ -264,6 +323,8 @@ def pgkq_fp16_decode_attn(q: torch.Tensor, K16: torch.Tensor, V16: torch.Tensor,
     """K16 [n_seq, n_kv, cap, d] fp16 rows; V16 the tiled value cache of the same shape."""
     n_seq, n_q, d = q.shape
     n_kv, cap = K16.shape[1], K16.shape[2]
+    _expect_shape(K16, (n_seq, n_kv, cap, d), "K16")
+    _expect_shape(V16, (n_seq, n_kv, cap, d), "V16")
     n_tok = cap if n_tokens is None else int(n_tokens)
     o = _opts(n_splits, events)
     if out is None:
@@ -294,10 +355,13 @@ def pgkq_kv_decode_attn(pk: PgkqParams, pv: PgkqParams, q: torch.Tensor, codes_k
                         n_splits: int = 0, out=None, workspace=None, events=None, stream=None):
     """Decode attention over key codes and value codes [n_seq, n_kv, capacity * record]."""
     n_seq, n_q, d = q.shape
+    _expect_codes(codes_k, n_seq * n_kv, capacity, pgkq_record_bytes(pk), "codes_k")
+    _expect_codes(codes_v, n_seq * n_kv, capacity, pgkq_record_bytes(pv), "codes_v")
     n_tok = capacity if n_tokens is None else int(n_tokens)
     o = _opts(n_splits, events)
     if out is None:
         out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    _expect_shape(out, (n_seq, n_q, d), "out")
     ck, cv = pk.c(), pv.c()
     nb = int(L.lib().pgkq_kv_decode_workspace_bytes(ctypes.byref(ck), ctypes.byref(cv), n_seq, n_q,
                                                      n_kv, n_tok, ctypes.byref(o)))
@@ -322,10 +386,13 @@ def pgkq_rtn_encode(K: torch.Tensor, bits: int, codes=None, capacity=None, token
                     stream=None):
     """K [n_seq, n_kv, n_tokens, d] (fp32 / fp16) -> codes [n_seq, n_kv, capacity * record] uint8."""
     n_seq, n_kv, n_tok, d = K.shape
-    cap = int(capacity) if capacity is not None else n_tok
+    rb = pgkq_rtn_record_bytes(d, bits)
     if codes is None:
-        rb = pgkq_rtn_record_bytes(d, bits)
+        cap = int(capacity) if capacity is not None else default_capacity(n_tok)
         codes = torch.zeros((n_seq, n_kv, cap * rb), dtype=torch.uint8, device=K.device)
+    else:
+        cap = int(capacity) if capacity is not None else _code_capacity(codes, n_seq * n_kv, rb)
+        _expect_codes(codes, n_seq * n_kv, cap, rb)
     st = L.lib().pgkq_rtn_encode(d, bits, _ptr(K), _dtype(K), n_seq, n_kv, n_tok, _ptr(codes), cap,
                                  int(token_offset), _stream(stream))
     L.check(st, "pgkq_rtn_encode")
@@ -345,10 +412,13 @@ def pgkq_rtn_decode_attn(q: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, 
     [n_seq, n_kv, cap, d]."""
     n_seq, n_q, d = q.shape
     n_kv, cap = V.shape[1], V.shape[2]
+    _expect_shape(V, (n_seq, n_kv, cap, d), "V")
+    _expect_codes(codes, n_seq * n_kv, cap, pgkq_rtn_record_bytes(d, bits))
     n_tok = cap if n_tokens is None else int(n_tokens)
     o = _opts(n_splits, events)
     if out is None:
         out = torch.empty((n_seq, n_q, d), dtype=torch.float32, device=q.device)
+    _expect_shape(out, (n_seq, n_q, d), "out")
     nb = int(L.lib().pgkq_rtn_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, ctypes.byref(o)))
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_rtn_decode_attn(d, bits, _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, cap,
@@ -362,9 +432,11 @@ def pgkq_rtn_logits(q: torch.Tensor, codes: torch.Tensor, n_kv: int, capacity: i
                     n_tokens=None, logits=None, workspace=None, stream=None):
     """Raw RTN logits [n_seq, n_q, n_tokens] fp32."""
     n_seq, n_q, d = q.shape
+    _expect_codes(codes, n_seq * n_kv, capacity, pgkq_rtn_record_bytes(d, bits))
     n_tok = capacity if n_tokens is None else int(n_tokens)
     if logits is None:
         logits = torch.empty((n_seq, n_q, n_tok), dtype=torch.float32, device=q.device)
+    _expect_shape(logits, (n_seq, n_q, n_tok), "logits")
     nb = int(L.lib().pgkq_rtn_decode_workspace_bytes(d, n_seq, n_q, n_kv, n_tok, None))
     ws, wsb = _ws(nb, q.device, workspace)
     st = L.lib().pgkq_rtn_logits(d, bits, _ptr(q), _dtype(q), n_seq, n_q, n_kv, n_tok, capacity,

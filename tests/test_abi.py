@@ -394,3 +394,55 @@ def test_pack_values_validation():
         assert f(n_streams=0, rows=0, cache=0) == L.PGKQ_OK
         assert f(cache=MIS) == L.PGKQ_ERR_ALIGN       # the tiled side moves 16-byte pieces
         assert f(rows=A + 1) == L.PGKQ_ERR_ALIGN      # fp16 rows: 2-byte aligned
+
+
+# ------------------------------------------------------------------ binding size checks
+# The C ABI sees pointers only, so the binding checks that a code buffer and a
+# value cache agree with the sizes the call implies, before anything is launched
+# (CPU tensors here: a passing check would only fail later, at the device-pointer
+# step, with a different message).
+
+def test_binding_rejects_mismatched_code_and_value_buffers():
+    import torch
+    p = api.PgkqParams(64, 3, 2, 64)
+    rb = api.pgkq_record_bytes(p)
+    n_seq, n_kv, n_q, d, cap = 2, 3, 6, 64, 64
+    q = torch.zeros((n_seq, n_q, d))
+    V = torch.zeros((n_seq, n_kv, cap, d), dtype=torch.float16)
+    good = torch.zeros((n_seq, n_kv, cap * rb), dtype=torch.uint8)
+    short = torch.zeros((n_seq, n_kv, (cap - 32) * rb), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="codes: .* bytes"):
+        api.pgkq_decode_attn(p, q, short, V, None, None, None, None)
+    with pytest.raises(ValueError, match="V: shape"):
+        api.pgkq_decode_attn(p, q, good, V[:, :, :, :32].contiguous(), None, None, None, None)
+    with pytest.raises(ValueError, match="codes: .* bytes"):
+        api.pgkq_estimate_logits(p, q, short, n_kv, cap, None, None, None, None)
+    with pytest.raises(ValueError, match="k_new: shape"):
+        api.pgkq_decode_step(p, q, torch.zeros((n_seq, n_kv + 1, d)), torch.zeros((n_seq, n_kv, d)),
+                             good, V, 0, None, None, None, None)
+    with pytest.raises(ValueError, match="codes: .* bytes"):
+        api.pgkq_decode_step(p, q, torch.zeros((n_seq, n_kv, d)),
+                             torch.zeros((n_seq, n_kv, d), dtype=torch.float16), short, V, 0,
+                             None, None, None, None)
+    K = torch.zeros((n_seq, n_kv, 40, d))
+    with pytest.raises(ValueError, match="codes: .* bytes"):
+        api.pgkq_encode(p, K, None, None, None, None, codes=short, capacity=cap)
+    with pytest.raises(ValueError, match="whole number"):
+        api.pgkq_encode(p, K, None, None, None, None, codes=good[:, :, :-1].contiguous())
+    pv = api.PgkqParams(64, 3, 2, 64, 0)
+    with pytest.raises(ValueError, match="codes_v: .* bytes"):
+        api.pgkq_kv_decode_attn(p, pv, q, good, short, n_kv, cap, None, None, None, None, None, None)
+    rtn_rb = api.pgkq_rtn_record_bytes(d, 4)
+    with pytest.raises(ValueError, match="codes: .* bytes"):
+        api.pgkq_rtn_decode_attn(q, torch.zeros((n_seq, n_kv, cap * rtn_rb - 4), dtype=torch.uint8),
+                                 V, 4)
+    with pytest.raises(ValueError, match="K16: shape"):
+        api.pgkq_fp16_decode_attn(q, torch.zeros((n_seq, n_kv, cap, 32), dtype=torch.float16), V)
+
+
+def test_binding_default_capacity_matches_the_value_cache():
+    # the key-code default and the value-cache default agree for ragged lengths
+    for T in (1, 31, 32, 33, 100, 512):
+        assert api.default_capacity(T) % 32 == 0
+        assert api.default_capacity(T) >= T
+        assert api.default_capacity(T) - T < 32 or T < 32
