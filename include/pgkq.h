@@ -18,8 +18,10 @@
  *
  * Conventions for every entry point:
  *  - Tensor pointers are DEVICE pointers unless the argument says "host".
- *    The caller owns all memory; the library allocates nothing and keeps no
- *    state between calls (calls are thread-safe).
+ *    The caller owns all memory; the library allocates no device memory and
+ *    keeps no device state between calls.  Its only state is a host-side
+ *    cache of the unit Lloyd-Max tables (a function of head_dim and b_main
+ *    alone, filled on first use under a mutex), so calls are thread-safe.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued asynchronously; results are valid after the stream syncs.
  *  - Arguments are validated on the host before anything is enqueued.  On an
@@ -108,7 +110,8 @@ const char* pgkq_version(void);
  * record size of the "Bit budget" paragraph).  0 if the parameters are invalid. */
 size_t pgkq_record_bytes(const pgkq_params* p);
 
-/* Bytes of a code buffer holding n_streams streams of `capacity` slots. */
+/* Bytes of a code buffer holding n_streams streams of `capacity` slots
+ * (record bytes of the "Bit budget" paragraph times slots times streams). */
 size_t pgkq_codes_bytes(const pgkq_params* p, int64_t n_streams, int64_t capacity);
 
 /* Host routine.  Lloyd-Max quantizer of rho = (r / ||k||) sqrt(d/2) under the
@@ -140,7 +143,8 @@ pgkq_status pgkq_lloyd_max_empirical(const double* samples_host, int64_t n_sampl
                                      int32_t b_main, double* levels_host,
                                      double* thresholds_host);
 
-/* Bytes of workspace pgkq_calibrate needs. */
+/* Bytes of workspace pgkq_calibrate needs (per-chunk float64 channel sums of
+ * the calibration keys that open the "PGKQ pipeline" paragraph). */
 size_t pgkq_calibrate_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_kv,
                                       int64_t n_tokens);
 
@@ -160,7 +164,8 @@ pgkq_status pgkq_calibrate(const pgkq_params* p, const void* K, pgkq_dtype k_dty
                            double* sumsq, uint16_t* perm, float* codebook, void* workspace,
                            size_t workspace_bytes, void* stream);
 
-/* Encode keys into the code buffer (steps (1)-(4)):
+/* Encode keys into the code buffer (steps (1)-(4) of the "PGKQ pipeline"
+ * paragraph; record layout as above, sized by the "Bit budget" paragraph):
  *   K      [n_seq][n_kv][n_tokens][d], dtype k_dtype (F32 or F16)
  *   codes  [n_seq][n_kv] streams of `capacity` slots; tokens are written to slots
  *          [token_offset, token_offset + n_tokens) of every stream, other slots
@@ -172,19 +177,26 @@ pgkq_status pgkq_encode(const pgkq_params* p, const void* K, pgkq_dtype k_dtype,
                         const float* codebook, const float* S, void* codes, int64_t capacity,
                         int64_t token_offset, void* stream);
 
-/* Bytes of workspace pgkq_decode_attn / pgkq_estimate_logits need. */
+/* Bytes of workspace pgkq_decode_attn / pgkq_estimate_logits need: the
+ * prepared queries (the Hadamard rotation of Q named in the throughput
+ * paragraph, with their lookup tables) and the split partial states. */
 size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_q,
                                    int64_t n_kv, int64_t n_tokens, const pgkq_launch_opts* opts);
 
-/* Decode attention over the compressed keys and fp16 values:
+/* Decode attention over the compressed keys and fp16 values (the end of the
+ * "PGKQ pipeline" paragraph: logits computed analytically from the codes,
+ * never from a rebuilt K; "Bit budget": V stays FP16):
  *   q     [n_seq][n_q][d], dtype q_dtype (F32, F16 or BF16); query head hq reads
  *         kv-head hq / (n_q / n_kv); n_q / n_kv must be 1, 2, 4 or 8
  *   codes as written by pgkq_encode, tokens [0, n_tokens) of each stream
  *   V     fp16 value cache in 32-token tiles (n_seq * n_kv streams of
  *         `capacity` slots, see the conventions above)
  *   out   [n_seq][n_q][d] fp32 = sum_t softmax_t(scale * logit_t) V_t
- * The weighted sum runs on the matrix cores with the softmax weights rounded
- * to fp16 (fp32 accumulation); the denominator sums the same rounded weights.
+ * The weighted sum runs on the matrix cores: each softmax weight p (at most
+ * 1) is split into two fp16 parts, hi = fp16(2^15 p) and lo = fp16(2^15 p -
+ * hi), both parts multiply the fp16 values exactly and the products
+ * accumulate in fp32 (the weight is carried to about 2^-22 relative); the
+ * denominator sums the fp32 weights themselves.
  *   softmax_scale <= 0 selects 1 / sqrt(d).
  * The logit of token t is
  *   sum_i level[rc_i] (q~[2i] cos thetahat[ac_i] + q~[2i+1] sin thetahat[ac_i])
@@ -200,7 +212,9 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
                              const pgkq_launch_opts* opts, void* workspace,
                              size_t workspace_bytes, void* stream);
 
-/* One decode step of a live cache: append the new token, then attend over it.
+/* One decode step of a live cache: append the new token, then attend over it
+ * (the decode loop of the Table III paragraph: each generated token's key is
+ * coded into the cache before the next logits are taken).
  * Encodes k_new [n_seq][n_kv][d] (k_dtype F32 or F16; steps (1)-(4), one key per
  * stream) into slot n_cached of every stream of `codes`, copies v_new
  * [n_seq][n_kv][d] fp16 into slot n_cached of the tiled V, then computes decode attention
@@ -229,8 +243,8 @@ pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype
                                  float* logits, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
-/* Write fp16 value rows into the 32-token-tile value cache (layout in the
- * conventions above):
+/* Write fp16 value rows into the 32-token-tile value cache (the FP16 V of the
+ * "Bit budget" paragraph; layout in the conventions above):
  *   rows   [n_streams][n_tokens][head_dim] fp16, plain rows (2-byte aligned)
  *   cache  n_streams streams of `capacity` slots (16-byte aligned);
  *          slots [slot_offset, slot_offset + n_tokens) are written, every
@@ -247,13 +261,14 @@ pgkq_status pgkq_unpack_values(const void* cache, int64_t n_streams, int64_t cap
                                int32_t head_dim, int64_t slot_offset, int64_t n_tokens, void* rows,
                                void* stream);
 
-/* Bytes of workspace pgkq_fp16_decode_attn needs. */
+/* Bytes of workspace pgkq_fp16_decode_attn needs (split partial states). */
 size_t pgkq_fp16_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q,
                                         int64_t n_kv, int64_t n_tokens,
                                         const pgkq_launch_opts* opts);
 
-/* Uncompressed comparator: decode attention on an fp16 key cache (the FP16
- * cache the pages take fidelity deltas against).
+/* Uncompressed comparator: decode attention on an fp16 key cache, the FP16
+ * cache of the throughput paragraph (232.16 tok/s there) and the reference
+ * of the fidelity deltas in the Table III paragraph.
  *   K16 [n_seq][n_kv][capacity][d] fp16 rows; V16 the fp16 value cache in
  *   32-token tiles (as for decode); q, out, scale as for decode. */
 pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_seq, int64_t n_q,
