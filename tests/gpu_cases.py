@@ -10,9 +10,12 @@ from oracle import attn, encode, layout
 from oracle.encode import Params
 from synth import make_inputs
 
-from parity_util import codebook_array, oracle_tables
+from parity_util import classify, codebook_array, merge_counts, oracle_tables
 
 DEV = "cuda:0"
+OUT_TOL = 1e-3     # attention outputs, max-abs
+LOGIT_TOL = 2e-3   # logits, in units of ||q|| ||k||
+GUARD = 4096       # bytes of guard band on each side of an output or workspace
 
 
 def params_of(cfg, hadamard=True) -> Params:
@@ -132,3 +135,97 @@ class Case:
             S=to_dev(self.S) if self.S is not None else None,
             V=v_cache(self.V, cap),
         )
+
+
+class Guarded:
+    """A device tensor of the given shape and dtype inside a larger byte buffer
+    whose GUARD bytes on either side are all-ones (NaN as fp16 / fp32): after a
+    call, `check()` asserts the kernels wrote nothing outside the tensor.  The
+    tensor itself starts out all-ones as well, so an element no kernel writes
+    stays NaN and fails the comparison."""
+
+    def __init__(self, shape, dtype):
+        n = 1
+        for s in shape:
+            n *= int(s)
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        self.raw = torch.full((2 * GUARD + nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+        self.nbytes = nbytes
+        self.t = self.raw[GUARD:GUARD + nbytes].view(dtype).view(*shape)
+
+    def check(self, what):
+        lo = self.raw[:GUARD]
+        hi = self.raw[GUARD + self.nbytes:]
+        assert bool(torch.all(lo == 0xFF)) and bool(torch.all(hi == 0xFF)), \
+            f"{what}: a kernel wrote outside its buffer"
+
+
+def gpu_encode(case, K=None):
+    import compressed_cache_decode_pgkq_amd as api
+    dev = case.dev_inputs()
+    Kt = k_tensor(case.K if K is None else K)
+    codes = api.pgkq_encode(lib_params(case.p), Kt, dev["signs"], dev["perm"], dev["codebook"],
+                            dev["S"], capacity=case.cap)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy()
+
+
+def code_counts(case, got):
+    f = case.oracle_fields()
+    counts = {}
+    n_seq, n_kv = case.K.shape[:2]
+    for b in range(n_seq):
+        for h in range(n_kv):
+            u = layout.unpack_stream(got[b, h], case.p, case.cap, case.T)
+            merge_counts(counts, classify(f[b][h], u, case.tables[h][1],
+                                          None if case.S is None else case.S[h], case.p))
+    return counts
+
+
+def logit_bound(case, b, hq, q=None):
+    q = case.q if q is None else q
+    G = q.shape[1] // case.K.shape[1]
+    qn = np.linalg.norm(q[b, hq].astype(np.float64))
+    kn = np.linalg.norm(case.K[b, hq // G].astype(np.float64), axis=1)
+    return LOGIT_TOL * qn * kn
+
+
+def check_decode(case, n_splits=0, q_override=None, q_dtype=None):
+    """Decode attention and the logit hook on the oracle's own code buffer against
+    the oracle; outputs, logits and workspaces sit between guard bands."""
+    import compressed_cache_decode_pgkq_amd as api
+    dev = case.dev_inputs()
+    p = lib_params(case.p)
+    q = case.q if q_override is None else q_override
+    qt = q_tensor(q, q_dtype or case.cfg.q_dtype)
+    codes = to_dev(case.oracle_codes())
+    n_seq, n_q, d = q.shape
+    n_kv = case.K.shape[1]
+    out = Guarded((n_seq, n_q, d), torch.float32)
+    lg = Guarded((n_seq, n_q, case.T), torch.float32)
+    nb = api.pgkq_decode_workspace_bytes(p, n_seq, n_q, n_kv, case.T, n_splits)
+    ws = Guarded((max(nb, 16),), torch.uint8)
+    nb_l = api.pgkq_decode_workspace_bytes(p, n_seq, n_q, n_kv, case.T, 0)
+    ws_l = Guarded((max(nb_l, 16),), torch.uint8)
+    api.pgkq_decode_attn(p, qt, codes, dev["V"], dev["signs"], dev["perm"], dev["codebook"],
+                         dev["S"], n_tokens=case.T, n_splits=n_splits, out=out.t, workspace=ws.t)
+    api.pgkq_estimate_logits(p, qt, codes, n_kv, case.cap, dev["signs"], dev["perm"],
+                             dev["codebook"], dev["S"], n_tokens=case.T, logits=lg.t, workspace=ws_l.t)
+    torch.cuda.synchronize()
+    for g, what in ((out, "out"), (lg, "logits"), (ws, "workspace"), (ws_l, "logit workspace")):
+        g.check(what)
+    ref, ref_lg = case.oracle_decode(q=q)
+    o = out.t.cpu().numpy()
+    l = lg.t.cpu().numpy()
+    err = float(np.max(np.abs(o - ref))) if o.size else 0.0
+    assert np.all(np.isfinite(o))
+    worst = 0.0
+    if case.T:
+        for b in range(n_seq):
+            for hq in range(n_q):
+                bound = logit_bound(case, b, hq, q)
+                worst = max(worst, float(np.max(np.abs(l[b, hq] - ref_lg[b, hq]) / bound)))
+    print(f"decode max-abs {err:.3e}  logit err / bound {worst:.3e}")
+    assert err <= OUT_TOL
+    assert worst <= 1.0
+    return o

@@ -16,13 +16,11 @@ import torch
 from oracle import attn, layout
 from synth import CONFIGS
 
-from gpu_cases import Case, k_tensor, lib_params, q_tensor, to_dev, v_cache, value_capacity
-from parity_util import assert_code_parity, classify, merge_counts
+from gpu_cases import (OUT_TOL, Case, check_decode, code_counts, gpu_encode, k_tensor, lib_params,
+                       q_tensor, to_dev, v_cache, value_capacity)
+from parity_util import assert_code_parity
 
 pytestmark = pytest.mark.gpu
-
-OUT_TOL = 1e-3
-LOGIT_TOL = 2e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -47,34 +45,12 @@ SMALL = {
 }
 
 
-def _gpu_encode(case, K=None):
-    api = _api()
-    dev = case.dev_inputs()
-    Kt = k_tensor(case.K if K is None else K)
-    codes = api.pgkq_encode(lib_params(case.p), Kt, dev["signs"], dev["perm"], dev["codebook"],
-                            dev["S"], capacity=case.cap)
-    torch.cuda.synchronize()
-    return codes.cpu().numpy()
-
-
-def _code_counts(case, got):
-    f = case.oracle_fields()
-    counts = {}
-    n_seq, n_kv = case.K.shape[:2]
-    for b in range(n_seq):
-        for h in range(n_kv):
-            u = layout.unpack_stream(got[b, h], case.p, case.cap, case.T)
-            merge_counts(counts, classify(f[b][h], u, case.tables[h][1],
-                                          None if case.S is None else case.S[h], case.p))
-    return counts
-
-
 @pytest.mark.parametrize("name", list(SMALL))
 def test_encode_codes_match_oracle(name):
     cfg, kw = SMALL[name]
     case = Case(cfg, **kw)
-    got = _gpu_encode(case)
-    counts = _code_counts(case, got)
+    got = gpu_encode(case)
+    counts = code_counts(case, got)
     print(name, counts)
     assert_code_parity(counts)
     if counts["mismatch"] == 0:
@@ -83,7 +59,7 @@ def test_encode_codes_match_oracle(name):
 
 def test_encode_without_hadamard():
     case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=500), hadamard=False)
-    counts = _code_counts(case, _gpu_encode(case))
+    counts = code_counts(case, gpu_encode(case))
     print(counts)
     assert_code_parity(counts)
 
@@ -123,67 +99,32 @@ def test_calibrate_matches_oracle(name):
     assert np.all(np.isinf(got[~fin]))
 
 
-def _logit_bound(case, b, hq):
-    G = case.cfg.n_q // case.cfg.n_kv
-    qn = np.linalg.norm(case.q[b, hq].astype(np.float64))
-    kn = np.linalg.norm(case.K[b, hq // G].astype(np.float64), axis=1)
-    return LOGIT_TOL * qn * kn
-
-
-def _check_decode(case, n_splits=0, q_override=None, q_dtype=None):
-    api = _api()
-    dev = case.dev_inputs()
-    p = lib_params(case.p)
-    q = case.q if q_override is None else q_override
-    qt = q_tensor(q, q_dtype or case.cfg.q_dtype)
-    codes = to_dev(case.oracle_codes())
-    out = api.pgkq_decode_attn(p, qt, codes, dev["V"], dev["signs"], dev["perm"], dev["codebook"],
-                               dev["S"], n_tokens=case.T, n_splits=n_splits)
-    lg = api.pgkq_estimate_logits(p, qt, codes, case.cfg.n_kv, case.cap, dev["signs"], dev["perm"],
-                                  dev["codebook"], dev["S"], n_tokens=case.T)
-    torch.cuda.synchronize()
-    ref, ref_lg = case.oracle_decode(q=q)
-    out = out.cpu().numpy()
-    lg = lg.cpu().numpy()
-    err = float(np.max(np.abs(out - ref))) if out.size else 0.0
-    n_seq, n_q = q.shape[:2]
-    worst = 0.0
-    for b in range(n_seq):
-        for hq in range(n_q):
-            bound = _logit_bound(case, b, hq)
-            worst = max(worst, float(np.max(np.abs(lg[b, hq] - ref_lg[b, hq]) / bound)) if case.T else 0)
-    print(f"decode max-abs {err:.3e}  logit err / bound {worst:.3e}")
-    assert err <= OUT_TOL
-    assert worst <= 1.0
-    return out
-
-
 @pytest.mark.parametrize("name", list(SMALL))
 @pytest.mark.parametrize("n_splits", [1, 0, 7, 12, 256])  # 12, 256: one partition per wavefront
 def test_decode_matches_oracle_on_identical_codes(name, n_splits):
     cfg, kw = SMALL[name]
-    _check_decode(Case(cfg, **kw), n_splits=n_splits)
+    check_decode(Case(cfg, **kw), n_splits=n_splits)
 
 
 @pytest.mark.parametrize("group", [1, 2, 4, 8])
 def test_decode_group_sizes(group):
     cfg = CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_kv=2, n_q=2 * group, n_tokens=600)
-    _check_decode(Case(cfg), n_splits=0)
+    check_decode(Case(cfg), n_splits=0)
 
 
 @pytest.mark.parametrize("qd", ["f32", "f16", "bf16"])
 def test_decode_query_dtypes(qd):
     case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=400))
     q = case.q.astype(np.float16).astype(np.float32) if qd == "f16" else case.q
-    _check_decode(case, q_override=q, q_dtype=qd)
+    check_decode(case, q_override=q, q_dtype=qd)
 
 
 @pytest.mark.parametrize("T", [1, 2, 63, 65, 257, 1000])
 def test_decode_ragged_lengths(T):
     case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=1000), n_tokens=T, capacity=1024)
-    _check_decode(case, n_splits=0)
-    _check_decode(case, n_splits=3)
-    _check_decode(case, n_splits=9)
+    check_decode(case, n_splits=0)
+    check_decode(case, n_splits=3)
+    check_decode(case, n_splits=9)
 
 
 def test_decode_empty_cache_gives_zeros():
@@ -205,15 +146,15 @@ def test_ablation_grid_hadamard_by_qjl(hadamard, qjl):
     every cell encodes bit-exactly and decodes within the bars."""
     cfg = CONFIGS["nano_b64_t512"].with_(n_seq=2, qjl_m=64 if qjl else 0)
     case = Case(cfg, hadamard=hadamard)
-    counts = _code_counts(case, _gpu_encode(case))
+    counts = code_counts(case, gpu_encode(case))
     print(hadamard, qjl, counts)
     assert_code_parity(counts)
-    _check_decode(case)
+    check_decode(case)
 
 
 def test_decode_without_hadamard():
     case = Case(CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=500), hadamard=False)
-    _check_decode(case)
+    check_decode(case)
 
 
 def test_end_to_end_calibrate_encode_decode():

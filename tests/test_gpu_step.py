@@ -71,10 +71,14 @@ STEP_CASES = {
     "d128_reorder": (CONFIGS["gqa_b16_t32k_encode"].with_(n_seq=1, n_tokens=500), {"reorder": True}),
     "d128_b4": (CONFIGS["gqa_b1_t131k"].with_(n_tokens=900), {}),
     "no_hadamard": (CONFIGS["gqa_b16_t32k"].with_(n_seq=1, n_tokens=400), {"hadamard": False}),
-    # the appending workgroups follow the n_q query-preparation workgroups of
-    # each sequence, one per kv-head: group sizes 2 and 8
+    # the preparation launch is a (sequence, row) grid: the appending
+    # workgroups take the first n_kv rows of each sequence, the query
+    # preparation the n_q rows after them; group sizes 1, 2 and 8, and more
+    # than two sequences so that the sequence axis of that grid is exercised
     "d128_g2": (CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_kv=4, n_q=8, n_tokens=200), {}),
     "d128_g8": (CONFIGS["gqa_b16_t32k"].with_(n_seq=2, n_kv=2, n_q=16, n_tokens=300), {}),
+    "d128_g1_5seq": (CONFIGS["gqa_b16_t32k"].with_(n_seq=5, n_kv=3, n_q=3, n_tokens=150), {}),
+    "d64_g4_3seq": (CONFIGS["nano_b64_t512"].with_(n_seq=3, n_kv=2, n_q=8, n_tokens=100), {}),
 }
 
 
