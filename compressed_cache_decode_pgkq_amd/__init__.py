@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     pgkq_calibrate_workspace_bytes,
     pgkq_codes_bytes,
     pgkq_decode_attn,
+    pgkq_decode_attn_noalloc,
     pgkq_decode_step,
     pgkq_decode_workspace_bytes,
     pgkq_encode,

@@ -20,6 +20,8 @@ PGKQ_ERR_ALIGN = 4
 PGKQ_ERR_WORKSPACE = 5
 PGKQ_ERR_HIP = 6
 
+PGKQ_NOALLOC_SCRATCH_BYTES = 8 << 20
+
 PGKQ_F32 = 0
 PGKQ_F16 = 1
 PGKQ_BF16 = 2
@@ -72,6 +74,8 @@ SIGNATURES = {
     "pgkq_decode_workspace_bytes": (_sz, [_P, _i64, _i64, _i64, _i64, _O]),
     "pgkq_decode_attn": (ctypes.c_int, [_P, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _vp,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _f32, _O, _vp, _sz, _vp]),
+    "pgkq_decode_attn_noalloc": (ctypes.c_int, [_P, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _O, _vp]),
     "pgkq_decode_step": (ctypes.c_int, [_P, _vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _i64, _i64,
                                         _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _f32, _O,
                                         _vp, _sz, _vp]),

@@ -223,6 +223,27 @@ def pgkq_decode_attn(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor, V
     return out
 
 
+def pgkq_decode_attn_noalloc(params: PgkqParams, q: torch.Tensor, codes: torch.Tensor,
+                             V: torch.Tensor, signs, perm, codebook, S, out: torch.Tensor,
+                             n_tokens=None, softmax_scale: float = 0.0, n_splits: int = 0,
+                             stream=None):
+    """pgkq_decode_attn with the library's built-in scratch as the workspace: the
+    caller passes inputs and `out` [n_seq, n_q, d] fp32; nothing is allocated."""
+    n_seq, n_q, d = q.shape
+    n_kv, cap = V.shape[1], V.shape[2]
+    _expect_shape(V, (n_seq, n_kv, cap, d), "V")
+    _expect_codes(codes, n_seq * n_kv, cap, pgkq_record_bytes(params))
+    _expect_shape(out, (n_seq, n_q, d), "out")
+    n_tok = cap if n_tokens is None else int(n_tokens)
+    o = _opts(n_splits, None)
+    st = L.lib().pgkq_decode_attn_noalloc(ctypes.byref(params.c()), _ptr(q), _dtype(q), n_seq, n_q,
+                                          n_kv, n_tok, cap, _ptr(signs), _ptr(perm), _ptr(codebook),
+                                          _ptr(S), _ptr(codes), _half(V), _ptr(out),
+                                          float(softmax_scale), ctypes.byref(o), _stream(stream))
+    L.check(st, "pgkq_decode_attn_noalloc")
+    return out
+
+
 def pgkq_decode_step(params: PgkqParams, q: torch.Tensor, k_new: torch.Tensor,
                      v_new: torch.Tensor, codes: torch.Tensor, V: torch.Tensor, n_cached: int,
                      signs, perm, codebook, S, softmax_scale: float = 0.0, n_splits: int = 0,

@@ -305,6 +305,34 @@ pgkq_status unit_table(int d, int bm, double* lv, double* th) {
   return PGKQ_OK;
 }
 
+// Built-in workspace of pgkq_decode_attn_noalloc: a static device array, one
+// copy per GPU (each holds it until the process ends).  Host code never uses
+// the array's name as an address: its device address on each GPU is looked up
+// once, with that GPU current, and kept in `ptr`.
+static_assert(PGKQ_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+__device__ __align__(256) unsigned char scratch[PGKQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct ScratchAddresses {
+  std::mutex mu;
+  void* ptr[kMaxDevices] = {};
+};
+ScratchAddresses g_scratch;
+
+pgkq_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PGKQ_ERR_HIP;
+  if (dev >= kMaxDevices) return PGKQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch.mu);
+  if (!g_scratch.ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PGKQ_ERR_HIP;
+    g_scratch.ptr[dev] = ptr;
+  }
+  *out = g_scratch.ptr[dev];
+  return PGKQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -471,10 +499,13 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
                                  const void* V, float* out, float* logits, float softmax_scale,
                                  const pgkq_launch_opts* opts, void* workspace,
                                  size_t workspace_bytes, void* stream,
-                                 const StepIn* step = nullptr) {
+                                 const StepIn* step = nullptr, bool builtin_scratch = false) {
   Geometry g;
   pgkq_status st = check_params(p, &g);
   if (st != PGKQ_OK) return st;
+  // the static scratch stands in for the workspace; its address is taken only
+  // once every argument has been validated
+  if (builtin_scratch) workspace_bytes = PGKQ_NOALLOC_SCRATCH_BYTES;
   if (step) {
     if (!step->k_new || !step->v_new) return PGKQ_ERR_NULL;
     if ((st = check_dtype(step->k_dtype, false)) != PGKQ_OK) return st;
@@ -482,7 +513,7 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
     if (step->slot < 0 || step->slot + 1 != n_tokens) return PGKQ_ERR_SHAPE;
   }
   const bool logits_mode = logits != nullptr;
-  if (!q || !signs || !codebook || !codes || !workspace) return PGKQ_ERR_NULL;
+  if (!q || !signs || !codebook || !codes || (!workspace && !builtin_scratch)) return PGKQ_ERR_NULL;
   if (!logits_mode && (!V || !out)) return PGKQ_ERR_NULL;
   if (g.m && !S) return PGKQ_ERR_NULL;
   if ((st = check_dtype(q_dtype, true)) != PGKQ_OK) return st;
@@ -494,12 +525,13 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   if (!logits_mode && capacity % kValueTile) return PGKQ_ERR_SHAPE;
   if (!fits_buffer(capacity, g.record_bytes(), g.d)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
-      !aligned16(workspace) || (perm && !aligned16(perm)) || (S && !aligned16(S)) ||
+      (!builtin_scratch && !aligned16(workspace)) || (perm && !aligned16(perm)) || (S && !aligned16(S)) ||
       (V && !aligned16(V)) || (out && !aligned16(out)) || (logits && !aligned16(logits)))
     return PGKQ_ERR_ALIGN;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
                                   opts ? opts->n_splits : 0);
   if (workspace_bytes < decode_ws(g, n_seq, n_q, sp)) return PGKQ_ERR_WORKSPACE;
+  if (builtin_scratch && (st = scratch_of_current_device(&workspace)) != PGKQ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_tokens == 0) {
     if (logits_mode) return PGKQ_OK;
@@ -580,6 +612,18 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
   return decode_common(p, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, signs, perm, codebook,
                        S, codes, V, out, nullptr, softmax_scale, opts, workspace, workspace_bytes,
                        stream);
+}
+
+pgkq_status pgkq_decode_attn_noalloc(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                                     int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                     int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                                     const float* codebook, const float* S, const void* codes,
+                                     const void* V, float* out, float softmax_scale,
+                                     const pgkq_launch_opts* opts, void* stream) {
+  if (!out) return PGKQ_ERR_NULL;
+  return decode_common(p, q, q_dtype, n_seq, n_q, n_kv, n_tokens, capacity, signs, perm, codebook,
+                       S, codes, V, out, nullptr, softmax_scale, opts, nullptr, 0, stream, nullptr,
+                       true);
 }
 
 pgkq_status pgkq_decode_step(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,

@@ -212,6 +212,27 @@ pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_d
                              const pgkq_launch_opts* opts, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Decode attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * pgkq_decode_attn without the workspace arguments.  The library's own scratch
+ * of PGKQ_NOALLOC_SCRATCH_BYTES (8 MiB) serves as the workspace: a static
+ * device array, one copy per GPU, held until the process ends; its address on
+ * the current device is looked up on the first call there (the stream must
+ * belong to the current device).  A call whose pgkq_decode_workspace_bytes()
+ * exceeds the scratch returns PGKQ_ERR_WORKSPACE before anything is enqueued
+ * (the 32k-token GQA cache of 16 x 32 query heads at 8 splits needs 3.2 MiB).
+ * Every call on one GPU uses the same scratch and leaves its contents there:
+ * calls that overlap on one GPU (other streams or threads) race.  Nothing in
+ * the scratch needs to start at zero.  Same validation, kernels and results
+ * as pgkq_decode_attn; allocates nothing. */
+#define PGKQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+pgkq_status pgkq_decode_attn_noalloc(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
+                                     int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
+                                     int64_t capacity, const int8_t* signs, const uint16_t* perm,
+                                     const float* codebook, const float* S, const void* codes,
+                                     const void* V, float* out, float softmax_scale,
+                                     const pgkq_launch_opts* opts, void* stream);
+
 /* One decode step of a live cache: append the new token, then attend over it
  * (the decode loop of the Table III paragraph: each generated token's key is
  * coded into the cache before the next logits are taken).

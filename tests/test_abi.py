@@ -446,3 +446,38 @@ def test_binding_default_capacity_matches_the_value_cache():
         assert api.default_capacity(T) % 32 == 0
         assert api.default_capacity(T) >= T
         assert api.default_capacity(T) - T < 32 or T < 32
+
+
+# ------------------------------------------------------------------ decode without allocation
+
+def _decode_noalloc(p=(128, 3, 2, 128, 1), q=A, n_seq=2, n_q=8, n_kv=2, n_tok=100, cap=128,
+                    signs=A, cb=A, S=A, codes=A, V=A, out=A, n_splits=0):
+    o = L.PgkqLaunchOpts(n_splits, None, None)
+    return L.lib().pgkq_decode_attn_noalloc(_params(*p), _vp(q) if q else None, L.PGKQ_BF16, n_seq,
+                                            n_q, n_kv, n_tok, cap, _vp(signs), None, _vp(cb),
+                                            _vp(S) if S else None, _vp(codes) if codes else None,
+                                            _vp(V) if V else None, _vp(out) if out else None, 0.0,
+                                            ctypes.byref(o), None)
+
+
+def test_decode_noalloc_validation_before_any_device_call():
+    assert _decode_noalloc(q=0) == L.PGKQ_ERR_NULL
+    assert _decode_noalloc(out=0) == L.PGKQ_ERR_NULL
+    assert _decode_noalloc(V=0) == L.PGKQ_ERR_NULL
+    assert _decode_noalloc(n_q=6) == L.PGKQ_ERR_UNSUPPORTED
+    assert _decode_noalloc(n_tok=129) == L.PGKQ_ERR_SHAPE
+    assert _decode_noalloc(out=MIS) == L.PGKQ_ERR_ALIGN
+    # a call whose workspace would exceed the built-in scratch is refused
+    p = api.PgkqParams(128, 3, 2, 128)
+    need = api.pgkq_decode_workspace_bytes(p, 64, 32, 8, 32768, 16)
+    assert need > L.PGKQ_NOALLOC_SCRATCH_BYTES
+    assert _decode_noalloc(n_seq=64, n_q=32, n_kv=8, n_tok=32768, cap=32768,
+                           n_splits=16) == L.PGKQ_ERR_WORKSPACE
+    # the benchmark's 32k-token cache fits
+    assert api.pgkq_decode_workspace_bytes(p, 16, 32, 8, 32768, 8) <= L.PGKQ_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define PGKQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.PGKQ_NOALLOC_SCRATCH_BYTES
