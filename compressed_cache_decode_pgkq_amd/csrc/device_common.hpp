@@ -32,6 +32,12 @@ __device__ __forceinline__ uint16_t buf_load_b16(__amdgpu_buffer_rsrc_t r, uint3
   return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kLoadStream));
 }
 
+// 32-bit store through a buffer resource: an offset at or beyond the range is
+// dropped by the buffer unit, so a lane stores or not without a branch.
+__device__ __forceinline__ void buf_store_b32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, kLoadStream);
+}
+
 // Compiler-only fence: emits no instruction, but no memory access is moved
 // across it and it closes a scheduling region.  Used to keep the scheduler
 // from hoisting every LDS table read of a long unrolled loop (register
@@ -42,6 +48,7 @@ __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 // derived from it cannot be hoisted above this line.
 __device__ __forceinline__ void pin_reg(uint32_t& v) { asm volatile("" : "+v"(v)::"memory"); }
 __device__ __forceinline__ void pin_reg(float& v) { asm volatile("" : "+v"(v)::"memory"); }
+__device__ __forceinline__ void pin_reg(double& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ float load_f(const void* p, int dtype, int64_t i) {
   if (dtype == DT_F32) return static_cast<const float*>(p)[i];

@@ -453,6 +453,7 @@ pgkq_status pgkq_encode(const pgkq_params* p, const void* K, pgkq_dtype k_dtype,
   if (token_offset + n_tokens > capacity) return PGKQ_ERR_SHAPE;
   if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;  // keeps every stream 4-byte aligned
   if ((n_tokens + 63) / 64 > 0x7FFFFFFF) return PGKQ_ERR_SHAPE;
+  if (!fits_buffer(capacity, g.record_bytes(), 0)) return PGKQ_ERR_SHAPE;
   if (!aligned16(K) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
       (perm && !aligned16(perm)) || (S && !aligned16(S)))
     return PGKQ_ERR_ALIGN;

@@ -145,6 +145,9 @@ def test_encode_validation():
     assert _encode(off=1) == L.PGKQ_ERR_SHAPE
     assert _encode(n_tok=-1) == L.PGKQ_ERR_SHAPE
     assert _encode(cap=15, n_tok=8) == L.PGKQ_ERR_SHAPE  # odd capacity with QJL
+    # a stream beyond the 32-bit range of the buffer stores (d64 b3 + QJL: 30 B a token)
+    assert _encode(cap=1 << 28, n_tok=0) == L.PGKQ_ERR_SHAPE
+    assert _encode(cap=1 << 27, n_tok=0) == L.PGKQ_OK
     assert _encode(K=MIS) == L.PGKQ_ERR_ALIGN
     assert _encode(codes=MIS) == L.PGKQ_ERR_ALIGN
     assert _encode(perm=MIS) == L.PGKQ_ERR_ALIGN
