@@ -182,6 +182,29 @@ def measure_copy(torch, dev, reps: int = 10) -> float:
     return 2 * n / (float(np.median(ts)) * 1e-3) / 1e9
 
 
+def measure_read(api, torch, dev, nbytes: int, flush, reps: int = 20) -> dict:
+    """Read ceiling: the library's read probe (16-byte non-temporal buffer loads,
+    the decode scans' load path, nothing else) over `nbytes` bytes, the
+    Infinity Cache evicted before each read; median GB/s of the kernel alone."""
+    nbytes = nbytes // 16 * 16
+    buf = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    acc = torch.zeros(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for r in range(reps + 3):
+        flush.fill_(r & 255)
+        e0.record()
+        api.pgkq_stream_read(buf, acc)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 3:
+            ts.append(e0.elapsed_time(e1))
+    del buf
+    ms = float(np.median(ts))
+    return {"bytes": nbytes, "ms": ms, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "p10_ms": float(np.percentile(ts, 10)), "p90_ms": float(np.percentile(ts, 90))}
+
+
 def run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E, reps: int = 20):
     """The same decode workload on the RTN INT4 / INT3 key caches, with PGKQ-coded
     values as well (PGKQ-KV k3v3), and on the uncompressed fp16 cache (same
@@ -408,6 +431,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="run only the library's read probe over the decode scan's algorithmic "
+                         "bytes, --steps times (the read ceiling, for rocprofv3)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU; use --gpus 1"}))
@@ -430,6 +456,15 @@ def main():
 
     import compressed_cache_decode_pgkq_amd as api
     from synth import CONFIGS
+
+    if args.read_probe:
+        c = CONFIGS["gqa_b16_t32k"]
+        rbp = api.pgkq_record_bytes(api.PgkqParams(c.head_dim, c.b_main, c.b_angle, c.qjl_m, 1))
+        nbytes = c.n_seq * c.n_kv * c.n_tokens * (rbp + 2 * c.head_dim)
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        res = measure_read(api, torch, dev, nbytes, flush, reps=args.steps)
+        print(json.dumps({"read_probe": res, "launches": args.steps + 3}))
+        return
 
     cfg = CONFIGS["gqa_b16_t32k"]           # decode workload
     ecfg = CONFIGS["gqa_b16_t32k_encode"]          # the same keys, encoded with the reorder step
@@ -501,6 +536,7 @@ def main():
     pct = lambda k: {"p10": float(np.percentile(ph[:, k], 10)), "p50": float(np.median(ph[:, k])),  # noqa: E731
                      "p90": float(np.percentile(ph[:, k], 90))}
     copy_gbs = measure_copy(torch, dev)
+    read = measure_read(api, torch, dev, n_seq * n_kv * T * (rb + 2 * d), flush)
     step_res = run_decode_step(api, torch, dev, cfg, p, q, K, V, codes, Vt, signs, perm, cb, S, ws,
                                flush, E)
     controls = run_controls(api, torch, dev, cfg, K, V, Vt, q, signs, S, flush, E)
@@ -582,7 +618,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_scan_kernel<128,3,QJL,G=4>", "launch_ms": scan_mean,
-                     "measured_copy_gbs": copy_gbs},
+                     "measured_copy_gbs": copy_gbs,
+                     # the same byte count read by the read probe (the scans'
+                     # load path and nothing else): the ceiling measured here
+                     "measured_read_gbs": read["gbs"],
+                     "frac_of_measured_read": achieved / read["gbs"]},
         "decode_step": step_res,
         "controls": controls,
         "other_workloads": others,

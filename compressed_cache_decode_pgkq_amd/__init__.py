@@ -32,6 +32,7 @@ from .api import (  # noqa: F401
     pgkq_rtn_logits,
     pgkq_rtn_record_bytes,
     pgkq_status_string,
+    pgkq_stream_read,
     pgkq_unpack_values,
     pgkq_version,
 )

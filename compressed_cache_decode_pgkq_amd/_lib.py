@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpgkq.so")
+# PGKQ_LIB names another build of the same ABI (the sanitized host-only build
+# of the validation layer that the CPU tests load); unset, the in-tree library.
+LIB_PATH = os.environ.get("PGKQ_LIB") or os.path.join(_HERE, "libpgkq.so")
 
 PGKQ_OK = 0
 PGKQ_ERR_NULL = 1
@@ -96,6 +98,7 @@ SIGNATURES = {
                                             _i64, _vp, _vp, _vp, _f32, _O, _vp, _sz, _vp]),
     "pgkq_rtn_logits": (ctypes.c_int, [_i32, _i32, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                        _vp, _vp, _vp, _sz, _vp]),
+    "pgkq_stream_read": (ctypes.c_int, [_vp, ctypes.c_uint64, _vp, _vp]),
 }
 
 

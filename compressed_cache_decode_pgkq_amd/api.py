@@ -464,3 +464,16 @@ def pgkq_rtn_logits(q: torch.Tensor, codes: torch.Tensor, n_kv: int, capacity: i
                                  _ptr(codes), _ptr(logits), _ptr(ws), wsb, _stream(stream))
     L.check(st, "pgkq_rtn_logits")
     return logits
+
+
+def pgkq_stream_read(src: torch.Tensor, xor_out=None, stream=None):
+    """Read probe: reads every byte of `src` the way the decode scans read the
+    cache and XORs its 32-bit words into `xor_out` (a one-element int32 device
+    tensor, zero-filled here when not given).  Returns `xor_out`."""
+    if xor_out is None:
+        xor_out = torch.zeros(1, dtype=torch.int32, device=src.device)
+    if _nbytes(xor_out) < 4:
+        raise ValueError("xor_out: needs one 32-bit word")
+    st = L.lib().pgkq_stream_read(_ptr(src), _nbytes(src), _ptr(xor_out), _stream(stream))
+    L.check(st, "pgkq_stream_read")
+    return xor_out

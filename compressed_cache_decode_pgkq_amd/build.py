@@ -1,8 +1,10 @@
 """Build the PGKQ HIP library (libpgkq.so) in-tree for gfx950.
 
-Every ``csrc/*.hip`` translation unit is compiled with hipcc in parallel and
-linked into ``compressed_cache_decode_pgkq_amd/libpgkq.so``.  Cross-compiles
-without a GPU.  Usage: ``python -m compressed_cache_decode_pgkq_amd.build``.
+Every ``csrc/*.hip`` translation unit (kernels and the device layer) is
+compiled with hipcc, every ``csrc/*.cpp`` one (the C-ABI layer: validation and
+planning, no HIP headers) with the host C++ compiler, in parallel, and linked
+into ``compressed_cache_decode_pgkq_amd/libpgkq.so``.  Cross-compiles without a
+GPU.  Usage: ``python -m compressed_cache_decode_pgkq_amd.build``.
 """
 
 from __future__ import annotations
@@ -31,6 +33,16 @@ CXXFLAGS = [
 ]
 
 
+HOST_CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
+
+
+def _host_cxx() -> str:
+    for c in (os.environ.get("CXX"), shutil.which("g++"), shutil.which("c++")):
+        if c and shutil.which(c):
+            return shutil.which(c)
+    raise RuntimeError("no host C++ compiler found (g++ required to build the C-ABI layer)")
+
+
 def _hipcc() -> str:
     for c in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if c and os.path.exists(c):
@@ -40,19 +52,22 @@ def _hipcc() -> str:
 
 def _compile(src: str, hipcc: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *CXXFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [_host_cxx(), *HOST_CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [hipcc, *CXXFLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"compile failed for {src}:\n{r.stderr}")
     return obj
 
 
 def build(verbose: bool = False, jobs: int | None = None) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, hipcc, verbose), srcs))

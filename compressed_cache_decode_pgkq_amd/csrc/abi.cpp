@@ -1,9 +1,9 @@
-// C-ABI host layer of the PGKQ library: argument validation, workspace
-// sizing, split selection and kernel dispatch, plus the host-side Lloyd-Max
-// codebook for the Beta radius prior.  See include/pgkq.h for the contract.
+// C-ABI layer of the PGKQ library: argument validation, workspace sizing,
+// split selection and the calls into the device layer, plus the host-side
+// Lloyd-Max codebook for the Beta radius prior.  See include/pgkq.h for the
+// contract.  Plain C++ (no HIP headers): every device action goes through the
+// dev_* functions of host_iface.hpp.
 #include "pgkq.h"
-
-#include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
@@ -11,7 +11,7 @@
 #include <mutex>
 #include <vector>
 
-#include "pgkq_internal.hpp"
+#include "host_iface.hpp"
 
 namespace {
 
@@ -54,7 +54,7 @@ pgkq_status check_group(int64_t n_q, int64_t n_kv, int* group) {
   return PGKQ_OK;
 }
 
-pgkq_status map_hip(hipError_t e) { return e == hipSuccess ? PGKQ_OK : PGKQ_ERR_HIP; }
+pgkq_status map_dev(int e) { return e == 0 ? PGKQ_OK : PGKQ_ERR_HIP; }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -125,19 +125,6 @@ size_t decode_ws(const Geometry& g, int64_t n_seq, int64_t n_q, const Splits& sp
 size_t fp16_ws(int d, int64_t n_seq, int64_t n_q, const Splits& sp) {
   if (sp.partials() <= 1) return 0;
   return round_up(size_t(n_seq) * n_q * sp.partials() * (d + 4) * sizeof(float), 256);
-}
-
-__global__ void zero_fill_kernel(float* p, size_t n) {
-  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-       i += size_t(gridDim.x) * blockDim.x)
-    p[i] = 0.f;
-}
-
-hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  const unsigned blocks = static_cast<unsigned>(std::min<size_t>((n + 255) / 256, 4096));
-  hipLaunchKernelGGL(zero_fill_kernel, dim3(blocks), dim3(256), 0, s, p, n);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- RTN control
@@ -305,32 +292,12 @@ pgkq_status unit_table(int d, int bm, double* lv, double* th) {
   return PGKQ_OK;
 }
 
-// Built-in workspace of pgkq_decode_attn_noalloc: a static device array, one
-// copy per GPU (each holds it until the process ends).  Host code never uses
-// the array's name as an address: its device address on each GPU is looked up
-// once, with that GPU current, and kept in `ptr`.
-static_assert(PGKQ_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
-__device__ __align__(256) unsigned char scratch[PGKQ_NOALLOC_SCRATCH_BYTES];
-
-constexpr int kMaxDevices = 64;
-struct ScratchAddresses {
-  std::mutex mu;
-  void* ptr[kMaxDevices] = {};
-};
-ScratchAddresses g_scratch;
-
-pgkq_status scratch_of_current_device(void** out) {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PGKQ_ERR_HIP;
-  if (dev >= kMaxDevices) return PGKQ_ERR_UNSUPPORTED;
-  std::lock_guard<std::mutex> lock(g_scratch.mu);
-  if (!g_scratch.ptr[dev]) {
-    void* ptr = nullptr;
-    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PGKQ_ERR_HIP;
-    g_scratch.ptr[dev] = ptr;
-  }
-  *out = g_scratch.ptr[dev];
-  return PGKQ_OK;
+// Device address of the built-in workspace of pgkq_decode_attn_noalloc on the
+// current device (looked up once per device by the device layer).
+pgkq_status scratch_address(void** out) {
+  const int e = pgkq::dev_scratch(out);
+  if (e == pgkq::kDevTooManyDevices) return PGKQ_ERR_UNSUPPORTED;
+  return e == 0 && *out ? PGKQ_OK : PGKQ_ERR_HIP;
 }
 
 }  // namespace
@@ -351,6 +318,14 @@ const char* pgkq_status_string(pgkq_status s) {
 }
 
 const char* pgkq_version(void) { return "pgkq-mi355x 0.1 (gfx950)"; }
+
+pgkq_status pgkq_stream_read(const void* src, uint64_t bytes, uint32_t* xor_out, void* stream) {
+  if (bytes == 0) return PGKQ_OK;
+  if (!src || !xor_out) return PGKQ_ERR_NULL;
+  if (bytes % 16 || bytes > (uint64_t(1) << 39)) return PGKQ_ERR_SHAPE;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(xor_out) & 3u)) return PGKQ_ERR_ALIGN;
+  return map_dev(pgkq::dev_stream_read(src, bytes, xor_out, stream));
+}
 
 size_t pgkq_record_bytes(const pgkq_params* p) {
   Geometry g;
@@ -435,7 +410,7 @@ pgkq_status pgkq_calibrate(const pgkq_params* p, const void* K, pgkq_dtype k_dty
   a.L = 1 << g.bm;
   st = unit_table(g.d, g.bm, a.base_levels, a.base_thresholds);
   if (st != PGKQ_OK) return st;
-  return map_hip(pgkq::launch_calibrate(a, static_cast<hipStream_t>(stream)));
+  return map_dev(pgkq::dev_calibrate(a, stream));
 }
 
 pgkq_status pgkq_encode(const pgkq_params* p, const void* K, pgkq_dtype k_dtype, int64_t n_seq,
@@ -473,7 +448,7 @@ pgkq_status pgkq_encode(const pgkq_params* p, const void* K, pgkq_dtype k_dtype,
   a.S = g.m ? S : nullptr;
   a.codes = static_cast<uint8_t*>(codes);
   a.stream_bytes = size_t(capacity) * g.record_bytes();
-  return map_hip(pgkq::launch_encode(g, a, static_cast<hipStream_t>(stream)));
+  return map_dev(pgkq::dev_encode(g, a, stream));
 }
 
 size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t n_q, int64_t n_kv,
@@ -532,11 +507,11 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
                                   opts ? opts->n_splits : 0);
   if (workspace_bytes < decode_ws(g, n_seq, n_q, sp)) return PGKQ_ERR_WORKSPACE;
-  if (builtin_scratch && (st = scratch_of_current_device(&workspace)) != PGKQ_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (builtin_scratch && (st = scratch_address(&workspace)) != PGKQ_OK) return st;
+  void* s = stream;
   if (n_tokens == 0) {
     if (logits_mode) return PGKQ_OK;
-    return map_hip(zero_fill(out, size_t(n_seq) * n_q * g.d, s));
+    return map_dev(pgkq::dev_zero_fill(out, size_t(n_seq) * n_q * g.d, s));
   }
   const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
   pgkq::DecodeArgs a{};
@@ -555,7 +530,7 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   a.S = g.m ? S : nullptr;
   a.codes = static_cast<const uint8_t*>(codes);
   a.stream_bytes = size_t(capacity) * g.record_bytes();
-  a.V = static_cast<const __half*>(V);
+  a.V = static_cast<const uint16_t*>(V);
   a.out = out;
   a.logits = logits;
   a.prep = static_cast<float*>(workspace);
@@ -577,28 +552,28 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
     a.append_slot = step->slot;
     a.k_new = step->k_new;
     a.k_dtype = static_cast<int>(step->k_dtype);
-    a.v_new = static_cast<const __half*>(step->v_new);
+    a.v_new = static_cast<const uint16_t*>(step->v_new);
     a.codes_w = static_cast<uint8_t*>(const_cast<void*>(codes));
-    a.V_w = static_cast<__half*>(const_cast<void*>(V));
+    a.V_w = static_cast<uint16_t*>(const_cast<void*>(V));
   }
-  hipError_t e = hipSuccess;
+  int e = 0;
   if (!a.fused_prep) {
-    e = pgkq::launch_query_prep(g, a, s);
-    if (e != hipSuccess) return PGKQ_ERR_HIP;
+    e = pgkq::dev_query_prep(g, a, s);
+    if (e != 0) return PGKQ_ERR_HIP;
   }
   if (opts && opts->scan_start) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_start, s) != 0)
       return PGKQ_ERR_HIP;
   }
-  e = pgkq::launch_decode_scan(g, a, logits_mode, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  e = pgkq::dev_decode_scan(g, a, logits_mode, s);
+  if (e != 0) return PGKQ_ERR_HIP;
   if (opts && opts->scan_stop) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_stop, s) != 0)
       return PGKQ_ERR_HIP;
   }
   if (!logits_mode && sp.partials() > 1) {
-    e = pgkq::launch_partial_merge(g.d, n_seq, n_q, sp.partials(), a.partial, out, s);
-    if (e != hipSuccess) return PGKQ_ERR_HIP;
+    e = pgkq::dev_partial_merge(g.d, n_seq, n_q, sp.partials(), a.partial, out, s);
+    if (e != 0) return PGKQ_ERR_HIP;
   }
   return PGKQ_OK;
 }
@@ -702,8 +677,8 @@ pgkq_status pgkq_kv_decode_attn(const pgkq_params* pk, const pgkq_params* pv, co
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
                                   opts ? opts->n_splits : 0);
   if (workspace_bytes < kv_ws(g, n_seq, n_q, sp)) return PGKQ_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (n_tokens == 0) return map_hip(zero_fill(out, size_t(n_seq) * n_q * g.d, s));
+  void* s = stream;
+  if (n_tokens == 0) return map_dev(pgkq::dev_zero_fill(out, size_t(n_seq) * n_q * g.d, s));
   const pgkq::PrepLayout pl{g.d, g.n(), 1 << g.ba, g.m};
   pgkq::DecodeArgs a{};
   a.q = q;
@@ -736,19 +711,19 @@ pgkq_status pgkq_kv_decode_attn(const pgkq_params* pk, const pgkq_params* pv, co
   a.stream_bytes_v = size_t(capacity) * gv.record_bytes();
   a.codebook_v = codebook_v;
   a.S_v = gv.m ? S_v : nullptr;
-  hipError_t e = pgkq::launch_query_prep(g, a, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  int e = pgkq::dev_query_prep(g, a, s);
+  if (e != 0) return PGKQ_ERR_HIP;
   if (opts && opts->scan_start) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_start, s) != 0)
       return PGKQ_ERR_HIP;
   }
-  e = pgkq::launch_kv_decode_scan(g, a, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  e = pgkq::dev_kv_decode_scan(g, a, s);
+  if (e != 0) return PGKQ_ERR_HIP;
   if (opts && opts->scan_stop) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_stop, s) != 0)
       return PGKQ_ERR_HIP;
   }
-  return map_hip(pgkq::launch_kv_merge(a, g.d, sp.partials(), s));
+  return map_dev(pgkq::dev_kv_merge(a, g.d, sp.partials(), s));
 }
 
 pgkq_status pgkq_estimate_logits(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
@@ -785,16 +760,15 @@ static pgkq_status values_common(const void* src, void* dst, int64_t n_streams, 
   if (!aligned16(unpack ? src : dst) || (reinterpret_cast<uintptr_t>(unpack ? dst : src) & 1u))
     return PGKQ_ERR_ALIGN;
   pgkq::ValuesArgs a{};
-  a.src = static_cast<const __half*>(src);
-  a.dst = static_cast<__half*>(dst);
+  a.src = static_cast<const uint16_t*>(src);
+  a.dst = static_cast<uint16_t*>(dst);
   a.n_streams = n_streams;
   a.n_tokens = n_tokens;
   a.capacity = capacity;
   a.slot_offset = slot_offset;
   a.d = head_dim;
   a.unpack = unpack;
-  return pgkq::launch_values(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PGKQ_OK
-                                                                               : PGKQ_ERR_HIP;
+  return map_dev(pgkq::dev_values(a, stream));
 }
 
 pgkq_status pgkq_pack_values(const void* rows, int64_t n_streams, int64_t n_tokens, int32_t head_dim,
@@ -832,8 +806,8 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
                                   opts ? opts->n_splits : 0);
   const size_t need = fp16_ws(head_dim, n_seq, n_q, sp);
   if (need && (!workspace || workspace_bytes < need)) return PGKQ_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (n_tokens == 0) return map_hip(zero_fill(out, size_t(n_seq) * n_q * head_dim, s));
+  void* s = stream;
+  if (n_tokens == 0) return map_dev(pgkq::dev_zero_fill(out, size_t(n_seq) * n_q * head_dim, s));
   pgkq::Fp16DecodeArgs a{};
   a.q = q;
   a.q_dtype = static_cast<int>(q_dtype);
@@ -844,8 +818,8 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   a.n_tokens = n_tokens;
   a.capacity = capacity;
   a.group = group;
-  a.K = static_cast<const __half*>(K16);
-  a.V = static_cast<const __half*>(V16);
+  a.K = static_cast<const uint16_t*>(K16);
+  a.V = static_cast<const uint16_t*>(V16);
   a.out = out;
   a.partial = static_cast<float*>(workspace);
   a.n_splits = sp.n;
@@ -854,17 +828,17 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   a.scale_log2 = scale * 1.4426950408889634f;
   if (opts && opts->scan_start) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_start, s) != 0)
       return PGKQ_ERR_HIP;
   }
-  hipError_t e = pgkq::launch_fp16_decode(a, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  int e = pgkq::dev_fp16_decode(a, s);
+  if (e != 0) return PGKQ_ERR_HIP;
   if (opts && opts->scan_stop) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_stop, s) != 0)
       return PGKQ_ERR_HIP;
   }
   if (sp.partials() > 1)
-    return map_hip(pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.partials(), a.partial, out, s));
+    return map_dev(pgkq::dev_partial_merge(head_dim, n_seq, n_q, sp.partials(), a.partial, out, s));
   return PGKQ_OK;
 }
 
@@ -898,7 +872,7 @@ pgkq_status pgkq_rtn_encode(int32_t head_dim, int32_t bits, const void* K, pgkq_
   a.token_offset = token_offset;
   a.codes = static_cast<uint8_t*>(codes);
   a.stream_bytes = size_t(capacity) * rtn_record(head_dim, bits);
-  return map_hip(pgkq::launch_rtn_encode(a, static_cast<hipStream_t>(stream)));
+  return map_dev(pgkq::dev_rtn_encode(a, stream));
 }
 
 size_t pgkq_rtn_decode_workspace_bytes(int32_t head_dim, int64_t n_seq, int64_t n_q, int64_t n_kv,
@@ -936,10 +910,10 @@ static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void*
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
                                   opts ? opts->n_splits : 0);
   if (workspace_bytes < rtn_ws(head_dim, group, n_seq, n_q, n_kv, sp)) return PGKQ_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* s = stream;
   if (n_tokens == 0) {
     if (logits_mode) return PGKQ_OK;
-    return map_hip(zero_fill(out, size_t(n_seq) * n_q * head_dim, s));
+    return map_dev(pgkq::dev_zero_fill(out, size_t(n_seq) * n_q * head_dim, s));
   }
   pgkq::RtnDecodeArgs a{};
   a.q = q;
@@ -954,7 +928,7 @@ static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void*
   a.group = group;
   a.codes = static_cast<const uint8_t*>(codes);
   a.stream_bytes = size_t(capacity) * rtn_record(head_dim, bits);
-  a.V = static_cast<const __half*>(V);
+  a.V = static_cast<const uint16_t*>(V);
   a.out = out;
   a.logits = logits;
   a.prep = static_cast<float*>(workspace);
@@ -966,21 +940,21 @@ static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void*
   a.wave_parts = sp.wave_parts;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = pgkq::launch_rtn_query_prep(a, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  int e = pgkq::dev_rtn_query_prep(a, s);
+  if (e != 0) return PGKQ_ERR_HIP;
   if (opts && opts->scan_start) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_start), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_start, s) != 0)
       return PGKQ_ERR_HIP;
   }
-  e = pgkq::launch_rtn_scan(a, logits_mode, s);
-  if (e != hipSuccess) return PGKQ_ERR_HIP;
+  e = pgkq::dev_rtn_scan(a, logits_mode, s);
+  if (e != 0) return PGKQ_ERR_HIP;
   if (opts && opts->scan_stop) {
-    if (hipEventRecord(static_cast<hipEvent_t>(opts->scan_stop), s) != hipSuccess)
+    if (pgkq::dev_record_event(opts->scan_stop, s) != 0)
       return PGKQ_ERR_HIP;
   }
   if (!logits_mode && sp.partials() > 1) {
-    e = pgkq::launch_partial_merge(head_dim, n_seq, n_q, sp.partials(), a.partial, out, s);
-    if (e != hipSuccess) return PGKQ_ERR_HIP;
+    e = pgkq::dev_partial_merge(head_dim, n_seq, n_q, sp.partials(), a.partial, out, s);
+    if (e != 0) return PGKQ_ERR_HIP;
   }
   return PGKQ_OK;
 }

@@ -108,7 +108,7 @@ __device__ __forceinline__ void append_key(const DecodeArgs& a, int64_t b, int h
   // from LDS); the angle grid is computed meanwhile
   int src = tid;
   bool neg = false;
-  __half vrow = __float2half(0.f);
+  uint16_t vrow = 0;  // fp16 bits
   if (tid < D) {
     s_raw[tid] = load_f(a.k_new, a.k_dtype, size_t(stream) * D + tid);
     vrow = a.v_new[size_t(stream) * D + tid];
@@ -419,10 +419,10 @@ hipError_t scan_t(const DecodeArgs& a, bool logits_mode, hipStream_t s) {
     if (a.fused_prep) {
       if (logits_mode) {
         hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, true, 0, true>), grid, dim3(kScanThreads),
-                           0, s, a, a.codes, a.V);
+                           0, s, a, a.codes, as_half(a.V));
       } else {
         hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, false, 0, true>), grid,
-                           dim3(kScanThreads), 0, s, a, a.codes, a.V);
+                           dim3(kScanThreads), 0, s, a, a.codes, as_half(a.V));
       }
       return hipGetLastError();
     }
@@ -430,10 +430,10 @@ hipError_t scan_t(const DecodeArgs& a, bool logits_mode, hipStream_t s) {
   if (a.fused_prep) return hipErrorInvalidValue;
   if (logits_mode) {
     hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, true>), grid, dim3(kScanThreads), 0, s, a,
-                       a.codes, a.V);
+                       a.codes, as_half(a.V));
   } else {
     hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, false>), grid, dim3(kScanThreads), 0, s,
-                       a, a.codes, a.V);
+                       a, a.codes, as_half(a.V));
   }
   return hipGetLastError();
 }

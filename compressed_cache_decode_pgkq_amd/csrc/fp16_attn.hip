@@ -184,9 +184,9 @@ template <int D, int G>
 hipError_t fp16_t(const Fp16DecodeArgs& a, hipStream_t s) {
   dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
   if (a.wave_parts) {
-    hipLaunchKernelGGL((fp16_scan_kernel<D, G, true>), grid, dim3(kThreads), 0, s, a, a.K, a.V);
+    hipLaunchKernelGGL((fp16_scan_kernel<D, G, true>), grid, dim3(kThreads), 0, s, a, as_half(a.K), as_half(a.V));
   } else {
-    hipLaunchKernelGGL((fp16_scan_kernel<D, G, false>), grid, dim3(kThreads), 0, s, a, a.K, a.V);
+    hipLaunchKernelGGL((fp16_scan_kernel<D, G, false>), grid, dim3(kThreads), 0, s, a, as_half(a.K), as_half(a.V));
   }
   return hipGetLastError();
 }

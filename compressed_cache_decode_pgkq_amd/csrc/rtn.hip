@@ -286,10 +286,10 @@ hipError_t scan_t(const RtnDecodeArgs& a, bool lm, hipStream_t s) {
   const dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
   if (lm) {
     hipLaunchKernelGGL((rtn_scan_kernel<D, BITS, G, true>), grid, dim3(kThreads), 0, s, a, a.codes,
-                       a.V);
+                       as_half(a.V));
   } else {
     hipLaunchKernelGGL((rtn_scan_kernel<D, BITS, G, false>), grid, dim3(kThreads), 0, s, a,
-                       a.codes, a.V);
+                       a.codes, as_half(a.V));
   }
   return hipGetLastError();
 }

@@ -385,6 +385,20 @@ pgkq_status pgkq_rtn_logits(int32_t head_dim, int32_t bits, const void* q, pgkq_
                             int64_t capacity, const void* codes, float* logits, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement utility (not a step of the method).  The decode scans are
+ * judged against the HBM bandwidth; besides the vendor figure, this reads a
+ * buffer the way they do (16-byte non-temporal buffer loads, one contiguous
+ * slice per workgroup, about 512 workgroups) and nothing else, so its rate is
+ * the read ceiling measured on the same device.
+ * ------------------------------------------------------------------------ */
+
+/* Read `bytes` bytes at `src` (device, 16-byte aligned, bytes a multiple of 16
+ * and at most 2^39) and XOR every 32-bit word of them into *xor_out (device,
+ * 4-byte aligned; the caller sets its initial value).  bytes == 0 is a no-op.
+ * Errors: PGKQ_ERR_NULL, PGKQ_ERR_SHAPE, PGKQ_ERR_ALIGN, PGKQ_ERR_HIP. */
+pgkq_status pgkq_stream_read(const void* src, uint64_t bytes, uint32_t* xor_out, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

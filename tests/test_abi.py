@@ -484,3 +484,69 @@ def test_noalloc_scratch_size_matches_the_header():
     src = open(HEADER).read()
     m = re.search(r"#define PGKQ_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == L.PGKQ_NOALLOC_SCRATCH_BYTES
+
+
+def test_stream_read_validation():
+    lib = L.lib()
+    assert lib.pgkq_stream_read(None, 0, None, None) == L.PGKQ_OK        # empty read: no-op
+    assert lib.pgkq_stream_read(None, 16, _vp(A), None) == L.PGKQ_ERR_NULL
+    assert lib.pgkq_stream_read(_vp(A), 16, None, None) == L.PGKQ_ERR_NULL
+    assert lib.pgkq_stream_read(_vp(A), 24, _vp(A), None) == L.PGKQ_ERR_SHAPE   # not 16-byte rows
+    assert lib.pgkq_stream_read(_vp(A), (1 << 39) + 16, _vp(A), None) == L.PGKQ_ERR_SHAPE
+    assert lib.pgkq_stream_read(_vp(MIS), 16, _vp(A), None) == L.PGKQ_ERR_ALIGN
+    assert lib.pgkq_stream_read(_vp(A), 16, _vp(A + 2), None) == L.PGKQ_ERR_ALIGN
+
+
+@pytest.mark.parametrize("n_seq,n_kv", [(1, 1), (1, 8), (16, 8), (64, 24), (200, 8)])
+def test_workspace_planning_sweep(n_seq, n_kv):
+    """Workspace sizes over token counts from 1 to 2^31 and requested split
+    counts from automatic to 4096: never zero for a valid shape, never smaller
+    than the query preparation plus one partial state per split actually used,
+    and monotone in the requested split count beyond the automatic plan."""
+    p = api.PgkqParams(128, 3, 2, 128)
+    n_q = 4 * n_kv
+    prep = n_seq * n_q * ((128 + 64 * 4 + 128 + 3) // 4 * 4) * 4
+    for T in (1, 63, 64, 65, 511, 4096, 32768, 131072, 1 << 31):
+        for ns in (0, 1, 2, 7, 8, 64, 256, 4096):
+            w = api.pgkq_decode_workspace_bytes(p, n_seq, n_q, n_kv, T, n_splits=ns)
+            assert w >= prep, (T, ns, w)
+            if ns == 1:
+                assert w < prep + 256, (T, w)   # one split: no partial states
+            wk = api.pgkq_kv_decode_workspace_bytes(p, api.PgkqParams(128, 3, 2, 128, 0),
+                                                    n_seq, n_q, n_kv, T, n_splits=ns)
+            assert wk >= prep, (T, ns, wk)
+            wf = api.pgkq_fp16_decode_workspace_bytes(128, n_seq, n_q, n_kv, T, n_splits=ns)
+            wr = api.pgkq_rtn_decode_workspace_bytes(128, n_seq, n_q, n_kv, T, n_splits=ns)
+            assert wf >= 0 and wr > 0
+
+
+def test_host_check_build_launches_only_valid_calls():
+    """Against the host-check build of the ABI layer (a stand-in device layer
+    that validates each argument block and counts the calls, launching
+    nothing): invalid calls reach no device call, and valid decode, encode and
+    logits calls over a range of shapes hand the device layer consistent plans.
+    The product library has no stand-in, so this test needs the host-check
+    build (tests/test_host_sanitized.py runs it there)."""
+    lib = L.lib()
+    if not hasattr(lib, "pgkq_hostcheck_calls"):
+        pytest.skip("needs the host-check build of the ABI layer")
+    calls = lib.pgkq_hostcheck_calls
+    calls.restype = ctypes.c_int
+    c0 = calls()
+    assert _decode(q=0) == L.PGKQ_ERR_NULL
+    assert _decode(n_q=6) == L.PGKQ_ERR_UNSUPPORTED
+    assert _decode(wsb=16) == L.PGKQ_ERR_WORKSPACE
+    assert _encode(n_tok=17) == L.PGKQ_ERR_SHAPE
+    assert _encode(K=MIS) == L.PGKQ_ERR_ALIGN
+    assert calls() == c0
+    for n_seq, n_kv, grp, T, ns in [(1, 8, 4, 131072, 0), (16, 8, 4, 32768, 8), (2, 2, 1, 100, 0),
+                                    (2, 2, 1, 100, 1), (3, 1, 8, 5000, 7), (1, 4, 2, 64, 4096)]:
+        cap = (T + 31) // 32 * 32
+        n_q = grp * n_kv
+        p = api.PgkqParams(128, 3, 2, 128)
+        need = api.pgkq_decode_workspace_bytes(p, n_seq, n_q, n_kv, T, n_splits=ns)
+        c1 = calls()
+        assert _decode(n_seq=n_seq, n_q=n_q, n_kv=n_kv, n_tok=T, cap=cap, wsb=need,
+                       n_splits=ns) == L.PGKQ_OK
+        assert calls() > c1
+    assert _encode(n_tok=16) == L.PGKQ_OK
