@@ -412,17 +412,25 @@ hipError_t prep_t(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Workgroups of the scan that prepares its query itself (one per stream): at
+// head_dim 64 two wavefronts, so that the many short streams of that shape are
+// resident at once (a 1536-stream, 512-token cache: one round instead of 1.2,
+// whose second round ran alone at one workgroup per CU), else four.
+template <int D>
+constexpr int kFusedWaves = D == 64 ? 2 : kScanWaves;
+
 template <int D, int BM, bool QJL, int G>
 hipError_t scan_t(const DecodeArgs& a, bool logits_mode, hipStream_t s) {
   dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
   if constexpr (G <= kFusedPrepMaxGroup) {
     if (a.fused_prep) {
+      constexpr int W = kFusedWaves<D>;
       if (logits_mode) {
-        hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, true, 0, true>), grid, dim3(kScanThreads),
-                           0, s, a, a.codes, as_half(a.V));
+        hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, true, 0, true, W>), grid,
+                           dim3(W * kWave), 0, s, a, a.codes, as_half(a.V));
       } else {
-        hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, false, 0, true>), grid,
-                           dim3(kScanThreads), 0, s, a, a.codes, as_half(a.V));
+        hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, false, 0, true, W>), grid,
+                           dim3(W * kWave), 0, s, a, a.codes, as_half(a.V));
       }
       return hipGetLastError();
     }

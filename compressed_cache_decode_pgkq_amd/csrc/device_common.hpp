@@ -31,6 +31,9 @@ __device__ __forceinline__ uint32_t buf_load_b32(__amdgpu_buffer_rsrc_t r, uint3
 __device__ __forceinline__ uint16_t buf_load_b16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return static_cast<uint16_t>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, kLoadStream));
 }
+__device__ __forceinline__ uint8_t buf_load_b8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return static_cast<uint8_t>(__builtin_amdgcn_raw_buffer_load_b8(r, static_cast<int>(off), 0, kLoadStream));
+}
 
 // 32-bit store through a buffer resource: an offset at or beyond the range is
 // dropped by the buffer unit, so a lane stores or not without a branch.

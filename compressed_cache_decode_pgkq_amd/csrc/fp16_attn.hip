@@ -173,6 +173,7 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
       sm.load_v(vc, c0, vrs, t_end);
     }
     const bool valid = c0 + prow < c_end;
+    sm.mask_v(vc, c0, t_end);
     sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], prow);
   }
   const size_t row0 = size_t(b) * a.n_q + size_t(h) * G;

@@ -80,6 +80,13 @@ struct MfmaPV {
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int n = 0; n < NT; ++n) vc.r[ks][n] = buf_load_b128(vr, base + ks * TILE_BYTES + n * 1024);
+  }
+
+  // Zero the value slots at or past t_end in a chunk that holds a ragged tile
+  // (they hold whatever the cache's spare slots hold).  Kept apart from the
+  // loads and called just before the chunk is used, so that issuing the loads
+  // never waits for them.
+  __device__ __forceinline__ void mask_v(VChunk& vc, int64_t c0, int64_t t_end) const {
     if (c0 + kWave > t_end && (t_end & 31) != 0) {  // wave-uniform: the chunk holds a ragged tile
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {

@@ -257,6 +257,7 @@ rtn_scan_kernel(RtnDecodeArgs a, const uint8_t* __restrict__ codes, const __half
           a.logits[(size_t(b) * a.n_q + size_t(h) * G + g) * a.n_tokens + t] = s[g];
       }
     } else {
+      sm.mask_v(vc, c0, t_end);
       sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0]);
     }
   }

@@ -66,20 +66,20 @@ __device__ __forceinline__ uint32_t code_at(const uint32_t* cw, int i) {
   return __builtin_amdgcn_alignbit(cw[w + 1], cw[w], s) & mask;
 }
 
-template <int D, int G, int VB, bool QJL>
-using ValuePath = std::conditional_t<(VB > 0), CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>,
-                                     MfmaPV<D, G, kScanWaves>>;
+template <int D, int G, int VB, bool QJL, int WAVES = kScanWaves>
+using ValuePath = std::conditional_t<(VB > 0), CodedPV<D, G, WAVES, (VB > 0 ? VB : 2), QJL>,
+                                     MfmaPV<D, G, WAVES>>;
 
 // Query preparation inside the scan (FUSED): used when every (sequence,
 // kv-head) stream is one workgroup, so that no preparation is repeated; the
 // results are bit-identical to the separate preparation kernel (same
 // operations in the same order).
-template <int D, int BM, bool QJL, int G>
+template <int D, int BM, bool QJL, int G, int NT = kScanThreads>
 struct FusedPrep {
   static constexpr int N = D / 2;
   static constexpr int A = 1 << (BM - 1);
   static constexpr int M = QJL ? D : 0;
-  static constexpr int TPR = QJL ? kScanThreads / (QJL ? M : 1) : 1;  // threads per row of S_h
+  static constexpr int TPR = QJL ? NT / (QJL ? M : 1) : 1;  // threads per row of S_h
   static constexpr int CPT = D / TPR;                                  // columns per thread
   static_assert(!QJL || TPR == 2 || TPR == 4, "rows of S_h per workgroup");
 
@@ -88,29 +88,65 @@ struct FusedPrep {
   float sq[QJL ? G : 1][QJL ? M : 1];
   double2 grid[A];   // (cos, sin) of the angle grid
 
-  __device__ __forceinline__ void run(const DecodeArgs& a, int64_t b, int h, int tid) {
-    constexpr int QE = (G * D + kScanThreads - 1) / kScanThreads;
+  static constexpr int QE = (G * D + NT - 1) / NT;
+
+  // The global loads of the preparation, issued before anything else of the
+  // workgroup (its first cache chunk among them, whose loads then queue behind
+  // these): the thread's slice of a row of S_h, its query elements as stored,
+  // their channel indices and signs.  All of them are unconditional buffer
+  // loads (a lane past the rows, or a missing channel order, reads zero
+  // through the range check), so that no branch or copy waits for one before
+  // the chunk's loads are issued.
+  struct Loads {
     float4 srow[QJL ? CPT / 4 : 1];
-    if constexpr (QJL) {  // the thread's slice of a row of S_h, first
+    uint32_t qlo[QE], qhi[QE];  // the element's low and high 16 bits (high: fp32 only)
+    uint32_t pidx[QE];          // the channel order's entry (0 without one)
+    uint32_t sgn[QE];           // the sign byte
+  };
+  __device__ __forceinline__ static void load(Loads& l, const DecodeArgs& a, int64_t b, int h,
+                                              int tid) {
+    if constexpr (QJL) {
       const float4* Sr = reinterpret_cast<const float4*>(a.S + (size_t(h) * M + tid / TPR) * D +
                                                          (tid % TPR) * CPT);
 #pragma unroll
-      for (int k = 0; k < CPT / 4; ++k) srow[k] = Sr[k];
+      for (int k = 0; k < CPT / 4; ++k) l.srow[k] = Sr[k];
     }
+    const uint32_t esz = a.q_dtype == DT_F32 ? 4u : 2u;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(
+        static_cast<const uint8_t*>(a.q) + (size_t(b) * a.n_q + size_t(h) * G) * D * esz, G * D * esz);
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.perm ? a.perm + size_t(h) * D : nullptr,
+                                                 a.perm ? 2u * D : 0u);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(a.signs + size_t(h) * D, D);
+#pragma unroll
+    for (int k = 0; k < QE; ++k) {
+      const int e = tid + k * NT;
+      const bool in = e < G * D;
+      const uint32_t c = static_cast<uint32_t>(e % D);
+      const uint32_t qo = in ? static_cast<uint32_t>(e) * esz : 0xFFFFFFF0u;
+      l.qlo[k] = buf_load_b16(qrs, qo);
+      l.qhi[k] = buf_load_b16(qrs, qo + 2);
+      l.pidx[k] = buf_load_b16(prs, in ? 2 * c : 0xFFFFFFF0u);
+      l.sgn[k] = buf_load_b8(srs, in ? c : 0xFFFFFFF0u);
+    }
+  }
+
+  __device__ __forceinline__ void run(const Loads& l, const DecodeArgs& a, int tid) {
     {
       float* qraw = reinterpret_cast<float*>(&q64[0][0]);
       int src[QE];
       float sgn[QE];
 #pragma unroll
       for (int k = 0; k < QE; ++k) {
-        const int e = tid + k * kScanThreads;
+        const int e = tid + k * NT;
         src[k] = 0;
         sgn[k] = 1.f;
         if (e < G * D) {
-          const int g = e / D, c = e % D;
-          qraw[e] = load_f(a.q, a.q_dtype, (size_t(b) * a.n_q + size_t(h) * G + g) * D + c);
-          src[k] = g * D + (a.perm ? int(a.perm[size_t(h) * D + c]) : c);
-          if (a.hadamard) sgn[k] = float(a.signs[size_t(h) * D + c]);
+          const uint32_t lo = l.qlo[k];
+          qraw[e] = a.q_dtype == DT_F32   ? __uint_as_float(lo | (l.qhi[k] << 16))
+                    : a.q_dtype == DT_F16 ? __half2float(__ushort_as_half(static_cast<uint16_t>(lo)))
+                                          : __uint_as_float(lo << 16);
+          src[k] = (e / D) * D + (a.perm ? int(l.pidx[k]) : e % D);
+          if (a.hadamard) sgn[k] = float(static_cast<int8_t>(l.sgn[k]));
         }
       }
       if (tid < A) {
@@ -121,7 +157,7 @@ struct FusedPrep {
       __syncthreads();
 #pragma unroll
       for (int k = 0; k < QE; ++k) {
-        const int e = tid + k * kScanThreads;
+        const int e = tid + k * NT;
         if (e < G * D) (&qf[0][0])[e] = qraw[src[k]] * sgn[k];
       }
       __syncthreads();
@@ -142,13 +178,13 @@ struct FusedPrep {
       }
       __syncthreads();
     } else if (a.hadamard) {
-      constexpr int BE = (G * N + kScanThreads - 1) / kScanThreads;
+      constexpr int BE = (G * N + NT - 1) / NT;
       for (int hh = 1; hh < D; hh <<= 1) {
         float u[BE], w[BE];
         int at[BE];
 #pragma unroll
         for (int k = 0; k < BE; ++k) {
-          const int e = tid + k * kScanThreads;
+          const int e = tid + k * NT;
           at[k] = -1;
           if (e < G * N) {
             const int g = e / N, j = e % N;
@@ -171,7 +207,7 @@ struct FusedPrep {
     const float sc = a.hadamard ? 1.0f / sqrtf(float(D)) : 1.0f;
 #pragma unroll
     for (int k = 0; k < QE; ++k) {
-      const int e = tid + k * kScanThreads;
+      const int e = tid + k * NT;
       if (e < G * D) (&q64[0][0])[e] = double((&qf[0][0])[e] * sc);
     }
     __syncthreads();
@@ -184,7 +220,7 @@ struct FusedPrep {
         double acc = 0.0;
 #pragma unroll
         for (int k = 0; k < CPT / 4; ++k) {
-          float4 v = srow[k];
+          float4 v = l.srow[k];
           pin_reg(v.x);  // converted where used, not all CPT doubles at once
           pin_reg(v.y);
           pin_reg(v.z);
@@ -208,10 +244,12 @@ struct FusedPrep {
   }
 };
 
-template <int D, int BM, bool QJL, int G, bool LOGITS, int VB = 0, bool FUSED = false>
-__global__ void __launch_bounds__(kScanThreads, kScanMinWavesPerEU)
+template <int D, int BM, bool QJL, int G, bool LOGITS, int VB = 0, bool FUSED = false,
+          int WAVES = kScanWaves>
+__global__ void __launch_bounds__(WAVES * kWave, kScanMinWavesPerEU)
 decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half* __restrict__ V) {
-  using VP = ValuePath<D, G, VB, QJL>;
+  constexpr int NT = WAVES * kWave;  // threads of the workgroup
+  using VP = ValuePath<D, G, VB, QJL, WAVES>;
   constexpr bool CODED_V = VB > 0;
   using SS = ScanShape<D, BM, G>;
   constexpr int N = SS::N, BA = SS::BA, P = SS::P, L = SS::L, A = SS::A, NCODES = SS::NCODES;
@@ -231,16 +269,16 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
 
   __shared__ __align__(16) float s_tab[MAIN_FLOATS];
   __shared__ __align__(16) float s_qt[NQT];
-  __shared__ __align__(16) float s_p[kScanWaves][kWave][G];
-  static_assert(CODED_V || sizeof(s_p[0]) >= MfmaPV<D, G, kScanWaves>::P_BYTES, "weight rows");
+  __shared__ __align__(16) float s_p[WAVES][kWave][G];
+  static_assert(CODED_V || sizeof(s_p[0]) >= MfmaPV<D, G, WAVES>::P_BYTES, "weight rows");
   // coded values: per-wavefront transposition blocks and the pair table
-  constexpr int VW_WORDS = CODED_V ? CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>::LDS_WORDS : 1;
+  constexpr int VW_WORDS = CODED_V ? CodedPV<D, G, WAVES, (VB > 0 ? VB : 2), QJL>::LDS_WORDS : 1;
   constexpr int VTAB = CODED_V ? (1 << (2 * VB - 1)) : 1;
-  __shared__ __align__(16) uint32_t s_vw[kScanWaves][VW_WORDS];
+  __shared__ __align__(16) uint32_t s_vw[WAVES][VW_WORDS];
   __shared__ __align__(16) float2 s_vtab[VTAB];
-  constexpr int P16 = CODED_V ? CodedPV<D, G, kScanWaves, (VB > 0 ? VB : 2), QJL>::P16_BYTES : 16;
-  __shared__ __align__(16) unsigned char s_p16[kScanWaves][P16];
-  using FP = FusedPrep<D, BM, QJL, (FUSED ? G : 1)>;
+  constexpr int P16 = CODED_V ? CodedPV<D, G, WAVES, (VB > 0 ? VB : 2), QJL>::P16_BYTES : 16;
+  __shared__ __align__(16) unsigned char s_p16[WAVES][P16];
+  using FP = FusedPrep<D, BM, QJL, (FUSED ? G : 1), NT>;
   __shared__ __align__(16) unsigned char s_fused_raw[FUSED ? sizeof(FP) : 16];
   FP& fp = *reinterpret_cast<FP*>(s_fused_raw);
 
@@ -279,7 +317,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   // is issued at its start; V is consumed only after the score, so its latency
   // hides behind the table lookups.
   uint32_t cw[NW];
-  float nu = 0.f;
+  uint16_t nu_bits = 0;  // fp16 residual norm, converted where it is used
   typename VP::VChunk vc;
   // lanes past the split end read neighbouring (or, past the stream, zero)
   // words; their scores are masked
@@ -287,24 +325,30 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
     const uint32_t t4 = static_cast<uint32_t>(c + lane) * 4u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) cw[w] = buf_load_b32(crs, t4 + w * row_bytes);
-    if constexpr (QJL) nu = half_bits_to_float(buf_load_b16(crs, nu_off + t4 / 2));
+    if constexpr (QJL) nu_bits = buf_load_b16(crs, nu_off + t4 / 2);
   };
 
-  if constexpr (FUSED) fp.run(a, b, h, tid);
+  // the preparation's own loads first, so that they do not queue behind the
+  // first chunk (loads return in order)
+  typename FP::Loads fl;
+  if constexpr (FUSED) FP::load(fl, a, b, h, tid);
+  float lvr[L];
+#pragma unroll
+  for (int r = 0; r < L; ++r) lvr[r] = lv[r];
 
   // Token ranges: either the workgroup's split is shared by its wavefronts in
   // interleaved chunks, or (wave_parts) every wavefront scans a contiguous
   // partition of it; either way the wavefronts are merged in the workgroup.
   int64_t c_first, c_end, c_step;
   if (a.wave_parts) {
-    const int64_t tpw = a.tokens_per_split / kScanWaves;
+    const int64_t tpw = a.tokens_per_split / WAVES;
     c_first = t_begin + int64_t(wave) * tpw;
     c_end = min<int64_t>(c_first + tpw, t_end);
     c_step = kWave;
   } else {
     c_first = t_begin + int64_t(wave) * kWave;
     c_end = t_end;
-    c_step = kScanThreads;
+    c_step = NT;
   }
   // With the query prepared here (one workgroup per stream, a long prologue)
   // the first chunk's loads are issued before the tables are built; with the
@@ -320,16 +364,15 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       }
     }
   };
-  if constexpr (EARLY) {
-    if (c_first < c_end) issue(c_first);
-  }
+  // unconditional (a wavefront without tokens reads zeros or unused words
+  // through the buffer ranges): a branch here would make the waits of the
+  // preparation below cover these loads too
+  if constexpr (EARLY) issue(c_first);
+  if constexpr (FUSED) fp.run(fl, a, tid);
 
   // ---- tables: one thread per (pair, query head)
   {
-    float lvr[L];
-#pragma unroll
-    for (int r = 0; r < L; ++r) lvr[r] = lv[r];
-    for (int ig = tid; ig < N * G; ig += kScanThreads) {
+    for (int ig = tid; ig < N * G; ig += NT) {
       const int i = ig / G, g = ig % G;
       float lt[A];
       if constexpr (FUSED) {
@@ -356,7 +399,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   if constexpr (CODED_V) {
     // (level_v[rc] cos thetahat[ac], level_v[rc] sin thetahat[ac]) per joint code
     constexpr int LV = 1 << VB, AV = 1 << (VB - 1);
-    for (int e = tid; e < LV * AV; e += kScanThreads) {
+    for (int e = tid; e < LV * AV; e += NT) {
       const int rc = e & (LV - 1), ac = e >> VB;
       double sn, cs;
       sincospi(-1.0 + (2.0 * ac + 1.0) / double(AV), &sn, &cs);
@@ -366,7 +409,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   }
   if constexpr (QJL) {
     const float kappa = 1.2533141373155003f / float(M);  // sqrt(pi/2) / m
-    for (int kg = tid; kg < (M / 4) * G; kg += kScanThreads) {
+    for (int kg = tid; kg < (M / 4) * G; kg += NT) {
       const int k = kg / G, g = kg % G;
       const float* sq = FUSED ? &fp.sq[g < (FUSED ? G : 1) ? g : 0][QJL && FUSED ? 4 * k : 0]
                               : prep0 + size_t(g) * pl.stride() + pl.off_sq() + 4 * k;
@@ -437,7 +480,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
         for (int g = 0; g < G; ++g) qs[g] += e[g];
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = fmaf(nu, qs[g], s[g]);
+      for (int g = 0; g < G; ++g) s[g] = fmaf(half_bits_to_float(nu_bits), qs[g], s[g]);
     }
 
     if constexpr (LOGITS) {
@@ -450,6 +493,7 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
       sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0], &s_vw[wave][0], s_vtab, c0, c_end,
                &s_p16[wave][0]);
     } else {
+      sm.mask_v(vc, c0, t_end);
       sm.chunk(s, valid, a.scale_log2, vc, &s_p[wave][0][0]);
     }
   }
