@@ -38,6 +38,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "decode_scan_gqa32k_b16_traffic.json")
 SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/scan.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/pgkq_internal.hpp",
+                "compressed_cache_decode_pgkq_amd/csrc/host_iface.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/coded_pv.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/mfma_pv.hpp",
                 "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
@@ -45,9 +46,10 @@ SCAN_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/scan.hpp",
 
 ENCODE_SOURCES = ["compressed_cache_decode_pgkq_amd/csrc/encode.hip",
                   "compressed_cache_decode_pgkq_amd/csrc/pgkq_internal.hpp",
+                  "compressed_cache_decode_pgkq_amd/csrc/host_iface.hpp",
                   "compressed_cache_decode_pgkq_amd/csrc/device_common.hpp"]
 PROFILE_UTIL = os.path.join(ROOT, "profiles", "utilization_gqa32k_b16.json")
-ENCODE_KERNEL = "void encode_kernel<128, 3, true, 2>"
+ENCODE_KERNEL = "void encode_kernel<128, 3, true, 2, true>"
 # vector ALU issue rate: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz (a
 # wave64 instruction occupies its SIMD for 4 clocks); an fp64 FMA is one
 # lane-operation, so this is also the published fp64 vector peak / 2
