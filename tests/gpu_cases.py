@@ -55,13 +55,13 @@ def value_capacity(T: int) -> int:
     return max(VALUE_TILE, -(-T // VALUE_TILE) * VALUE_TILE)
 
 
-def tile_values(V, cap):
+def tile_values(V, cap, spare=0.0):
     """Rows V [n_seq, n_kv, T, d] -> an [n_seq, n_kv, cap, d] fp16 array whose memory is the
     32-token-tile value cache: element (t, c) at half-word
     (t/32) 32 d + ((c/16) 4 + (t%32)/8) 128 + (c%16) 8 + t%8 of its stream.
-    Slots past T are zero."""
+    Slots past T hold `spare`."""
     n_seq, n_kv, T, d = V.shape
-    buf = np.zeros((n_seq, n_kv, cap, d), dtype=np.float16)
+    buf = np.full((n_seq, n_kv, cap, d), spare, dtype=np.float16)
     buf[:, :, :T] = V
     # t = 32 a + 8 b + e, c = 16 f + g  ->  order (a, f, b, g, e)
     x = buf.reshape(n_seq, n_kv, cap // 32, 4, 8, d // 16, 16).transpose(0, 1, 2, 5, 3, 6, 4)
@@ -76,17 +76,18 @@ def untile_values(buf, T=None):
     return rows if T is None else rows[:, :, :T]
 
 
-def v_cache(V, cap):
-    """Device copy of the tiled value cache of rows V."""
-    return to_dev(tile_values(np.asarray(V, dtype=np.float16), cap))
+def v_cache(V, cap, spare=0.0):
+    """Device copy of the tiled value cache of rows V (slots past the rows hold `spare`)."""
+    return to_dev(tile_values(np.asarray(V, dtype=np.float16), cap, spare))
 
 
 class Case:
     """Oracle-side encoding of a workload plus its device copies."""
 
     def __init__(self, cfg, n_tokens=None, capacity=None, reorder=False, hadamard=True,
-                 inputs=None):
+                 inputs=None, v_spare=0.0):
         self.cfg = cfg
+        self.v_spare = v_spare  # value of the cache's spare slots on the device
         self.p = params_of(cfg, hadamard)
         inp = inputs if inputs is not None else make_inputs(cfg)
         T = cfg.n_tokens if n_tokens is None else n_tokens
@@ -133,7 +134,7 @@ class Case:
             perm=to_dev(self.perm.astype(np.uint16).view(np.int16)) if self.perm_arg is not None else None,
             codebook=to_dev(self.cb),
             S=to_dev(self.S) if self.S is not None else None,
-            V=v_cache(self.V, cap),
+            V=v_cache(self.V, cap, self.v_spare),
         )
 
 

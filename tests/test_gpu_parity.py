@@ -127,6 +127,24 @@ def test_decode_ragged_lengths(T):
     check_decode(case, n_splits=9)
 
 
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 129, 200])
+@pytest.mark.parametrize("variant", ["b3_qjl_g1", "b3_qjl_g2", "b4_g1"])
+def test_decode_ragged_lengths_d64(T, variant):
+    """head_dim 64: one workgroup per stream (two wavefronts, the query prepared
+    in the scan; the first chunk requested before the preparation computes,
+    ragged tiles masked at use) and split launches, on every tail shape."""
+    base = CONFIGS["nano_t128"].with_(n_tokens=200)
+    if variant == "b3_qjl_g2":
+        base = base.with_(n_kv=12, n_q=24)
+    elif variant == "b4_g1":
+        base = base.with_(b_main=4, b_angle=3, qjl_m=0)
+    # spare value slots hold NaN: a ragged tile's tail must be masked, not weighted by 0
+    case = Case(base, n_tokens=T, capacity=224, v_spare=np.nan)
+    check_decode(case, n_splits=0)
+    check_decode(case, n_splits=1)
+    check_decode(case, n_splits=3)
+
+
 def test_decode_empty_cache_gives_zeros():
     api = _api()
     case = Case(CONFIGS["nano_t128"], n_tokens=0, capacity=128)
