@@ -336,6 +336,44 @@ def run_nano_latency(api, torch, dev, E, reps: int = 50):
             "note": "cache-resident, launch-bound: latency only"}
 
 
+def decode_only(api, torch, dev, name: str, calls: int) -> dict:
+    """Only the decode call of one named workload, `calls` times with the
+    Infinity Cache evicted before each (for a rocprofv3 kernel trace of the
+    call's launches: query preparation, scan, merge)."""
+    from synth import CONFIGS, make_inputs
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg)
+    n_seq, n_kv, T, d = inp["K"].shape
+    p = api.PgkqParams(d, cfg.b_main, cfg.b_angle, cfg.qjl_m, 1)
+    K = torch.from_numpy(inp["K"]).to(dev)
+    Vt = api.pgkq_pack_values(torch.from_numpy(inp["V"]).to(dev))
+    q = torch.from_numpy(inp["q"]).to(dev)
+    if cfg.q_dtype == "bf16":
+        q = q.to(torch.bfloat16)
+    signs = torch.from_numpy(inp["signs"]).to(dev)
+    S = torch.from_numpy(inp["S"]).to(dev) if cfg.qjl_m else None
+    _, _, cb = api.pgkq_calibrate(p, K)
+    codes = api.pgkq_encode(p, K, signs, None, cb, S, capacity=T)
+    del K
+    out = torch.empty((n_seq, cfg.n_q, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(api.pgkq_decode_workspace_bytes(p, n_seq, cfg.n_q, n_kv, T, cfg.n_splits),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for r in range(calls + 3):
+        flush.fill_(r & 255)
+        e0.record()
+        api.pgkq_decode_attn(p, q, codes, Vt, signs, None, cb, S, n_splits=cfg.n_splits, out=out,
+                             workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 3:
+            ts.append(e0.elapsed_time(e1))
+    return {"workload": name, "description": cfg.description, "calls": calls + 3,
+            "call_ms_p50": float(np.median(ts))}
+
+
 def run_other_workloads(api, torch, dev, flush, E, reps: int = 20):
     """Decode of the other configurations of the pages' workload list on this
     GPU (NanoGPT-256 context with and without QJL, the 131k-token single
@@ -433,6 +471,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration for rocprofv3)")
+    ap.add_argument("--decode-only", metavar="WORKLOAD", default=None,
+                    help="run only the decode call of one named workload (e.g. gqa_b1_t131k), "
+                         "--steps times, for a rocprofv3 kernel trace of its launches")
     ap.add_argument("--read-probe", action="store_true",
                     help="run only the library's read probe over the decode scan's algorithmic "
                          "bytes, --steps times (the read ceiling, for rocprofv3)")
@@ -458,6 +499,10 @@ def main():
 
     import compressed_cache_decode_pgkq_amd as api
     from synth import CONFIGS
+
+    if args.decode_only:
+        print(json.dumps(decode_only(api, torch, dev, args.decode_only, args.steps)))
+        return
 
     if args.read_probe:
         c = CONFIGS["gqa_b16_t32k"]
