@@ -421,7 +421,7 @@ constexpr int kFusedWaves = D == 64 ? 2 : kScanWaves;
 
 template <int D, int BM, bool QJL, int G>
 hipError_t scan_t(const DecodeArgs& a, bool logits_mode, hipStream_t s) {
-  dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
+  dim3 grid(unsigned(a.n_kv), unsigned(a.n_seq), unsigned(a.n_splits));
   if constexpr (G <= kFusedPrepMaxGroup) {
     if (a.fused_prep) {
       constexpr int W = kFusedWaves<D>;

@@ -83,7 +83,11 @@ struct DecodeArgs {
   float* prep;          // workspace: query prep
   float* partial;       // workspace: partial states [n_seq][n_q][n_splits][d + 4]
   int n_splits;         // workgroups per (sequence, kv-head)
-  int64_t tokens_per_split;
+  int64_t tokens_per_split;  // tokens of a split (of a leading split when n_lead > 0)
+  // Front-loaded splits: splits [0, n_lead) hold tokens_per_split tokens, the
+  // rest tail_split tokens each (n_lead = 0: every split tokens_per_split)
+  int n_lead;
+  int64_t tail_split;
   int wave_parts;       // 1: each wavefront scans a contiguous partition of the split
   int fused_prep;       // 1: the scan prepares the query itself (one workgroup per stream)
   float scale_log2;     // softmax scale * log2(e)

@@ -100,7 +100,7 @@ kv_merge_kernel(const float* __restrict__ partial, float* __restrict__ out, cons
 
 template <int D, int BM, bool QJL, int G, int VB>
 hipError_t kv_t(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
+  dim3 grid(unsigned(a.n_kv), unsigned(a.n_seq), unsigned(a.n_splits));
   hipLaunchKernelGGL((decode_scan_kernel<D, BM, QJL, G, false, VB>), grid, dim3(kScanThreads), 0, s,
                      a, a.codes, as_half(a.V));
   return hipGetLastError();

@@ -283,15 +283,21 @@ decode_scan_kernel(DecodeArgs a, const uint8_t* __restrict__ codes, const __half
   FP& fp = *reinterpret_cast<FP*>(s_fused_raw);
 
   const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  // grid (kv-head, sequence, split): split-major dispatch order, so that the
+  // leading (larger) splits of every stream run first
+  const int split = blockIdx.z;
+  const int h = blockIdx.x;
+  const int64_t b = blockIdx.y;
   const PrepLayout pl{D, N, A, M};
   const float* lv = a.codebook + size_t(h) * 2 * L;
   const float* prep0 = a.prep + (size_t(b) * a.n_q + size_t(h) * G) * pl.stride();
 
-  const int64_t t_begin = int64_t(split) * a.tokens_per_split;
-  const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
+  const bool trailing = split >= a.n_lead && a.n_lead > 0;
+  const int64_t t_begin = trailing ? int64_t(a.n_lead) * a.tokens_per_split +
+                                         int64_t(split - a.n_lead) * a.tail_split
+                                   : int64_t(split) * a.tokens_per_split;
+  const int64_t t_end =
+      min<int64_t>(t_begin + (trailing ? a.tail_split : a.tokens_per_split), a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
   const uint8_t* cbase = codes + size_t(stream) * a.stream_bytes;
   // buffer ranges: the whole code stream, and this stream's V rows [0, t_end)

@@ -203,7 +203,10 @@ size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t 
  *   + sqrt(pi/2)/m * nu_t * sum_j (S_h q~)_j (2 bit_tj - 1),
  * with q~ the query through the kv-head's transform.  The token range is split
  * across workgroups (flash-decoding); partial states are merged with a
- * log-sum-exp merge.  Workspace: pgkq_decode_workspace_bytes(). */
+ * log-sum-exp merge.  The split sizes are the library's choice (splits that
+ * run first are given more tokens than the last ones); a requested count
+ * above 65535 after the library's rounding, or a plan that would need one,
+ * returns PGKQ_ERR_SHAPE.  Workspace: pgkq_decode_workspace_bytes(). */
 pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
                              int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,
                              int64_t capacity, const int8_t* signs, const uint16_t* perm,

@@ -26,6 +26,16 @@ void check_decode(const pgkq::Geometry& g, const pgkq::DecodeArgs& a) {
   require(a.stream_bytes == size_t(a.capacity) * g.record_bytes(), "decode: stream bytes");
   require(a.n_splits >= 1 && a.tokens_per_split >= 64, "decode: split plan");
   require(int64_t(a.n_splits) * a.tokens_per_split >= a.n_tokens, "decode: splits cover the tokens");
+  if (a.n_lead > 0) {  // front-loaded sizes: they cover the tokens and no split is empty
+    const int64_t lead = int64_t(a.n_lead) * a.tokens_per_split;
+    require(a.n_lead < a.n_splits && a.tail_split >= 64 && a.tokens_per_split >= a.tail_split,
+            "decode: front-loaded sizes");
+    require(lead + int64_t(a.n_splits - a.n_lead) * a.tail_split >= a.n_tokens,
+            "decode: front-loaded splits cover the tokens");
+    require(lead + int64_t(a.n_splits - a.n_lead - 1) * a.tail_split < a.n_tokens,
+            "decode: every front-loaded split holds a token");
+  }
+  require(a.n_splits <= 65535, "decode: splits fit the grid");
   require(a.group * a.n_kv == a.n_q, "decode: query-head groups");
   require(a.prep && a.partial && a.codes && a.signs && a.codebook, "decode: pointers");
 }

@@ -550,3 +550,13 @@ def test_host_check_build_launches_only_valid_calls():
                        n_splits=ns) == L.PGKQ_OK
         assert calls() > c1
     assert _encode(n_tok=16) == L.PGKQ_OK
+
+
+def test_split_count_beyond_the_grid_is_rejected():
+    # 16 777 184 tokens at one partition per 256 tokens: 65 536 splits, one more
+    # than a grid dimension holds
+    cap = (1 << 24) - 32
+    p = api.PgkqParams(64, 3, 2, 64)
+    assert _decode(p=(64, 3, 2, 64, 1), n_seq=1, n_q=2, n_kv=2, n_tok=cap, cap=cap,
+                   n_splits=1 << 20) == L.PGKQ_ERR_SHAPE
+    assert api.pgkq_decode_workspace_bytes(p, 1, 2, 2, cap, n_splits=1 << 20) > 0
