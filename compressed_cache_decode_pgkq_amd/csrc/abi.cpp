@@ -850,6 +850,7 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
     return PGKQ_ERR_ALIGN;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
                                   opts ? opts->n_splits : 0);
+  if (sp.n > kMaxGridYZ) return PGKQ_ERR_SHAPE;  // splits are a grid dimension
   const size_t need = fp16_ws(head_dim, n_seq, n_q, sp);
   if (need && (!workspace || workspace_bytes < need)) return PGKQ_ERR_WORKSPACE;
   void* s = stream;
@@ -871,6 +872,14 @@ pgkq_status pgkq_fp16_decode_attn(const void* q, pgkq_dtype q_dtype, int64_t n_s
   a.n_splits = sp.n;
   a.tokens_per_split = sp.tokens_per;
   a.wave_parts = sp.wave_parts;
+  {
+    const SplitSizes fl = front_load(sp, n_tokens);
+    if (fl.n_lead > 0) {
+      a.n_lead = fl.n_lead;
+      a.tokens_per_split = fl.lead;
+      a.tail_split = fl.tail;
+    }
+  }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   a.scale_log2 = scale * 1.4426950408889634f;
   if (opts && opts->scan_start) {
@@ -955,6 +964,7 @@ static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void*
     return PGKQ_ERR_ALIGN;
   const Splits sp = choose_splits(n_seq * n_kv, std::max<int64_t>(n_tokens, 1),
                                   opts ? opts->n_splits : 0);
+  if (sp.n > kMaxGridYZ) return PGKQ_ERR_SHAPE;  // splits are a grid dimension
   if (workspace_bytes < rtn_ws(head_dim, group, n_seq, n_q, n_kv, sp)) return PGKQ_ERR_WORKSPACE;
   void* s = stream;
   if (n_tokens == 0) {
@@ -984,6 +994,14 @@ static pgkq_status rtn_decode_common(int32_t head_dim, int32_t bits, const void*
   a.n_splits = sp.n;
   a.tokens_per_split = sp.tokens_per;
   a.wave_parts = sp.wave_parts;
+  {
+    const SplitSizes fl = front_load(sp, n_tokens);
+    if (fl.n_lead > 0) {
+      a.n_lead = fl.n_lead;
+      a.tokens_per_split = fl.lead;
+      a.tail_split = fl.tail;
+    }
+  }
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(head_dim));
   a.scale_log2 = scale * 1.4426950408889634f;
   int e = pgkq::dev_rtn_query_prep(a, s);

@@ -71,9 +71,10 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
   static_assert(sizeof(s_p[0]) >= MfmaPV<D, G, kWaves>::P_BYTES, "weight rows");
 
   const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  // grid (kv-head, sequence, split): split-major, leading (larger) splits first
+  const int split = blockIdx.z;
+  const int h = blockIdx.x;
+  const int64_t b = blockIdx.y;
 
   SM sm;
   sm.init(tid);
@@ -91,8 +92,12 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
   const int my_row = kb & (NIT - 1);          // row of the chunk this lane ends up scoring
   const int prow = my_row * TPI + slot;       // its token index within the chunk
 
-  const int64_t t_begin = int64_t(split) * a.tokens_per_split;
-  const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
+  const bool trailing = split >= a.n_lead && a.n_lead > 0;
+  const int64_t t_begin = trailing ? int64_t(a.n_lead) * a.tokens_per_split +
+                                         int64_t(split - a.n_lead) * a.tail_split
+                                   : int64_t(split) * a.tokens_per_split;
+  const int64_t t_end =
+      min<int64_t>(t_begin + (trailing ? a.tail_split : a.tokens_per_split), a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
   const __amdgpu_buffer_rsrc_t krs =
       make_rsrc(K + size_t(stream) * a.capacity * D, static_cast<uint32_t>(t_end * D * 2));
@@ -183,7 +188,7 @@ fp16_scan_kernel(Fp16DecodeArgs a, const __half* __restrict__ K, const __half* _
 
 template <int D, int G>
 hipError_t fp16_t(const Fp16DecodeArgs& a, hipStream_t s) {
-  dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
+  dim3 grid(unsigned(a.n_kv), unsigned(a.n_seq), unsigned(a.n_splits));
   if (a.wave_parts) {
     hipLaunchKernelGGL((fp16_scan_kernel<D, G, true>), grid, dim3(kThreads), 0, s, a, as_half(a.K), as_half(a.V));
   } else {

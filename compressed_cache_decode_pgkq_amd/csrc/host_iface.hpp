@@ -120,6 +120,8 @@ struct Fp16DecodeArgs {
   float* partial;
   int n_splits;
   int64_t tokens_per_split;
+  int n_lead;            // front-loaded splits, as in DecodeArgs
+  int64_t tail_split;
   int wave_parts;       // 1: each wavefront scans a contiguous partition of the split
   float scale_log2;
 };
@@ -153,6 +155,8 @@ struct RtnDecodeArgs {
   float* partial;       // workspace: partial states
   int n_splits;
   int64_t tokens_per_split;
+  int n_lead;            // front-loaded splits, as in DecodeArgs
+  int64_t tail_split;
   int wave_parts;
   float scale_log2;
 };

@@ -198,13 +198,18 @@ rtn_scan_kernel(RtnDecodeArgs a, const uint8_t* __restrict__ codes, const __half
   static_assert(sizeof(s_p[0]) >= MfmaPV<D, G, kWaves>::P_BYTES, "weight rows");
 
   const int tid = threadIdx.x;
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  // grid (kv-head, sequence, split): split-major, leading (larger) splits first
+  const int split = blockIdx.z;
+  const int h = blockIdx.x;
+  const int64_t b = blockIdx.y;
   const float* qrow = a.prep + (size_t(b) * a.n_kv + h) * rtn_prep_stride(D, G);
 
-  const int64_t t_begin = int64_t(split) * a.tokens_per_split;
-  const int64_t t_end = min<int64_t>(t_begin + a.tokens_per_split, a.n_tokens);
+  const bool trailing = split >= a.n_lead && a.n_lead > 0;
+  const int64_t t_begin = trailing ? int64_t(a.n_lead) * a.tokens_per_split +
+                                         int64_t(split - a.n_lead) * a.tail_split
+                                   : int64_t(split) * a.tokens_per_split;
+  const int64_t t_end =
+      min<int64_t>(t_begin + (trailing ? a.tail_split : a.tokens_per_split), a.n_tokens);
   const int64_t stream = b * a.n_kv + h;
   const __amdgpu_buffer_rsrc_t crs =
       make_rsrc(codes + size_t(stream) * a.stream_bytes, static_cast<uint32_t>(a.stream_bytes));
@@ -284,7 +289,7 @@ hipError_t encode_t(const RtnEncodeArgs& a, hipStream_t s) {
 
 template <int D, int BITS, int G>
 hipError_t scan_t(const RtnDecodeArgs& a, bool lm, hipStream_t s) {
-  const dim3 grid(unsigned(a.n_splits), unsigned(a.n_kv), unsigned(a.n_seq));
+  const dim3 grid(unsigned(a.n_kv), unsigned(a.n_seq), unsigned(a.n_splits));
   if (lm) {
     hipLaunchKernelGGL((rtn_scan_kernel<D, BITS, G, true>), grid, dim3(kThreads), 0, s, a, a.codes,
                        as_half(a.V));
