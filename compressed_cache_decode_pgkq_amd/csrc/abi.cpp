@@ -88,7 +88,14 @@ constexpr int kScanWaves = 4;
 // A requested count is honoured as the number of partial states merged per
 // query head; when its partitions are short (at most 1024 tokens) each
 // workgroup runs four consecutive partitions, one per wavefront, sharing one
-// build of the lookup tables.
+// build of the lookup tables.  A split holds at most kMaxSplitTokens tokens
+// (more splits are used when the request would give longer ones): a lane then
+// adds at most 1024 weights and 1024 weighted rows into its fp32 state, so a
+// long run of equal terms, whose rounding errors all have the same sign,
+// stays inside the output tolerance (over 16 777 184 identical tokens one
+// split drifted by 1.1e-2, splits of 2^20 tokens by 1.2e-3).
+constexpr int64_t kMaxSplitTokens = int64_t(1) << 18;
+
 Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested,
                      bool allow_wave_parts = true) {
   if (requested == 0 && allow_wave_parts && n_units < 64) {
@@ -110,8 +117,9 @@ Splits choose_splits(int64_t n_units, int64_t n_tokens, int32_t requested,
   ns = std::min<int64_t>(std::max<int64_t>(ns, 1), max_ns);
   int64_t tps = (n_tokens + ns - 1) / ns;
   tps = std::max<int64_t>(64, round_up(static_cast<size_t>(tps), 64));
+  tps = std::min<int64_t>(tps, kMaxSplitTokens);
   ns = std::max<int64_t>(1, (n_tokens + tps - 1) / tps);
-  return Splits{static_cast<int>(ns), tps, 0};
+  return Splits{static_cast<int>(std::min<int64_t>(ns, 0x7FFFFFFF)), tps, 0};
 }
 
 // Front-loaded split sizes for the scans whose workgroups interleave over one
@@ -136,6 +144,7 @@ SplitSizes front_load(const Splits& sp, int64_t n_tokens) {
   tail = static_cast<int64_t>(round_up(static_cast<size_t>(tail), 64));
   const int64_t lead = 3 * tail;
   if (int64_t(nl) * lead + int64_t(nt - 1) * tail >= n_tokens) return z;  // a split would be empty
+  if (lead > kMaxSplitTokens) return z;
   z.n_lead = nl;
   z.lead = lead;
   z.tail = tail;
@@ -527,7 +536,8 @@ static pgkq_status decode_common(const pgkq_params* p, const void* q, pgkq_dtype
   if (n_tokens < 0 || capacity < 1 || n_tokens > capacity) return PGKQ_ERR_SHAPE;
   if (g.m && (capacity & 1)) return PGKQ_ERR_SHAPE;
   if (!logits_mode && capacity % kValueTile) return PGKQ_ERR_SHAPE;
-  if (!fits_buffer(capacity, g.record_bytes(), g.d)) return PGKQ_ERR_SHAPE;
+  // the logit hook reads no value rows: only its code stream has to fit
+  if (!fits_buffer(capacity, g.record_bytes(), logits_mode ? 0 : g.d)) return PGKQ_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(signs) || !aligned16(codebook) || !aligned16(codes) ||
       (!builtin_scratch && !aligned16(workspace)) || (perm && !aligned16(perm)) || (S && !aligned16(S)) ||
       (V && !aligned16(V)) || (out && !aligned16(out)) || (logits && !aligned16(logits)))

@@ -204,8 +204,9 @@ size_t pgkq_decode_workspace_bytes(const pgkq_params* p, int64_t n_seq, int64_t 
  * with q~ the query through the kv-head's transform.  The token range is split
  * across workgroups (flash-decoding); partial states are merged with a
  * log-sum-exp merge.  The split sizes are the library's choice (splits that
- * run first are given more tokens than the last ones); a requested count
- * above 65535 after the library's rounding, or a plan that would need one,
+ * run first are given more tokens than the last ones, and no split holds more
+ * than 2^18 tokens: a smaller requested count is raised to keep the fp32
+ * accumulation of one split short); a plan with more than 65535 splits
  * returns PGKQ_ERR_SHAPE.  Workspace: pgkq_decode_workspace_bytes(). */
 pgkq_status pgkq_decode_attn(const pgkq_params* p, const void* q, pgkq_dtype q_dtype,
                              int64_t n_seq, int64_t n_q, int64_t n_kv, int64_t n_tokens,

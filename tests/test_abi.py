@@ -510,8 +510,12 @@ def test_workspace_planning_sweep(n_seq, n_kv):
         for ns in (0, 1, 2, 7, 8, 64, 256, 4096):
             w = api.pgkq_decode_workspace_bytes(p, n_seq, n_q, n_kv, T, n_splits=ns)
             assert w >= prep, (T, ns, w)
-            if ns == 1:
+            if ns == 1 and T <= 1 << 18:
                 assert w < prep + 256, (T, w)   # one split: no partial states
+            if ns == 1 and T > 1 << 18:
+                # a split holds at most 2^18 tokens: the request is raised
+                n = -(-T // (1 << 18))
+                assert w >= prep + n_seq * n_q * n * (128 + 4) * 4, (T, w)
             wk = api.pgkq_kv_decode_workspace_bytes(p, api.PgkqParams(128, 3, 2, 128, 0),
                                                     n_seq, n_q, n_kv, T, n_splits=ns)
             assert wk >= prep, (T, ns, wk)
@@ -550,6 +554,16 @@ def test_host_check_build_launches_only_valid_calls():
                        n_splits=ns) == L.PGKQ_OK
         assert calls() > c1
     assert _encode(n_tok=16) == L.PGKQ_OK
+    # the logit hook at a code stream of 58 040 098 74-byte records (4.0 GiB):
+    # accepted, while decode attention needs the value rows to fit as well
+    cap = 0xFFFFFFF0 // 74 // 2 * 2
+    c1 = calls()
+    st = lib.pgkq_estimate_logits(_params(128, 4, 3, 128, 1), _vp(A), L.PGKQ_F32, 1, 4, 1, cap, cap,
+                                  _vp(A), None, _vp(A), _vp(A), _vp(A), _vp(A), _vp(A), 1 << 30, None)
+    assert st == L.PGKQ_OK and calls() > c1
+    cap32 = cap // 32 * 32   # a whole number of value tiles: rejected for the value range only
+    assert _decode(p=(128, 4, 3, 128, 1), n_seq=1, n_q=4, n_kv=1, n_tok=cap32, cap=cap32,
+                   wsb=1 << 30) == L.PGKQ_ERR_SHAPE
 
 
 def test_split_count_beyond_the_grid_is_rejected():
