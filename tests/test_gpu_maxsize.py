@@ -1,4 +1,4 @@
-"""GPU parity at the largest streams the C ABI accepts.
+"""GPU parity at the largest streams and batches the C ABI accepts.
 
 The scans address one stream's codes and value rows with 32-bit byte offsets
 (buffer resources), so the library rejects a stream whose codes or values
@@ -10,9 +10,12 @@ tokens at the start, across the 2 GiB mark and at the very end:
   range (capacity x 256 bytes, 32-token tiles);
 * the logit hook over one stream of 58 040 098 tokens (d128, b4/3 + QJL,
   74-byte records): its codes end within 16 bytes of the largest accepted
-  range.
+  range;
+* decode attention over 65 535 sequences, the most a grid dimension holds
+  (the sequence index is one of the scan's grid dimensions), at one and at
+  three splits per stream.
 
-Every key is one of two fixed keys ("cold" everywhere, "hot" in three 64-token
+In the first two, every key is one of two fixed keys ("cold" everywhere, "hot" in three 64-token
 blocks: at the start, across 2^31 bytes of the stream, at the end), so the
 oracle needs only those two keys: their codes (compared word by word at the
 hot blocks and at random cold tokens), their logits, and the attention output
@@ -199,3 +202,59 @@ def test_logits_at_the_largest_code_stream():
         err = np.abs(got - ref[:, col:col + 1]) / (qn[:, None] * kn[col])
         print(f"{'hot' if col else 'cold'}: max error {err.max():.2e} of ||q|| ||k||", flush=True)
         assert err.max() <= LOGIT_TOL
+
+
+
+@pytest.mark.parametrize("T,n_splits", [(40, 0), (200, 3)])
+def test_decode_with_the_most_sequences(T, n_splits):
+    """65 535 sequences (a grid dimension at its limit) of one kv-head with two
+    query heads, d64, b3/2 + QJL: the scan's grid is (kv-head, sequence,
+    split), the preparation's (sequence, query head).  One workgroup per
+    stream at 40 tokens, three splits at 200.  Codes and outputs of 96 sampled
+    sequences (the first two, the last two and random ones) against the
+    oracle."""
+    import compressed_cache_decode_pgkq_amd as api
+    from parity_util import assert_code_parity, classify, merge_counts
+    n_seq, n_kv, n_q, d = 65535, 1, 2, 64
+    p = Params(d, 3, 2, d, True)
+    rng = np.random.default_rng(7170 + T)
+    scale = np.exp(0.5 * rng.standard_normal(d)).astype(np.float32)
+    K = rng.standard_normal((n_seq, n_kv, T, d), dtype=np.float32)
+    K *= scale
+    V = rng.standard_normal((n_seq, n_kv, T, d), dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((n_seq, n_q, d), dtype=np.float32)
+    signs = np.where(rng.random((n_kv, d)) < 0.5, -1, 1).astype(np.int8)
+    S = rng.standard_normal((n_kv, d, d), dtype=np.float32)
+    sumsq = np.zeros(d)
+    for b0 in range(0, n_seq, 4096):
+        sumsq += calibrate.channel_sumsq(K[b0:b0 + 4096, 0])
+    c, t = codebook.lloyd_max_beta(d, 3)
+    lv, th = codebook.scaled_table(c, t, calibrate.head_scale(sumsq, n_seq * T), d)
+    cb = codebook.pack_table(lv, th)[None].astype(np.float32)
+    print(f"T {T}, splits {n_splits}: inputs ready", flush=True)
+
+    lp = api.PgkqParams(d, 3, 2, d, 1)
+    d_signs, d_S, d_cb = (torch.as_tensor(x, device=DEV) for x in (signs, S, cb))
+    cap = -(-T // 32) * 32
+    dK = torch.as_tensor(K, device=DEV)
+    codes = api.pgkq_encode(lp, dK, d_signs, None, d_cb, d_S, capacity=cap)
+    del dK
+    Vt = api.pgkq_pack_values(torch.as_tensor(V, device=DEV), capacity=cap)
+    out = api.pgkq_decode_attn(lp, torch.as_tensor(q, device=DEV), codes, Vt, d_signs, None, d_cb,
+                               d_S, n_tokens=T, n_splits=n_splits)
+    torch.cuda.synchronize()
+
+    pick = np.unique(np.concatenate([[0, 1, n_seq - 2, n_seq - 1],
+                                     rng.choice(n_seq, 92, replace=False)]))
+    pick_t = torch.as_tensor(pick, device=DEV)
+    f = encode.encode_cache(K[pick], signs, None, [(lv, th)], S, p)
+    counts = {}
+    got_codes = codes[pick_t].cpu().numpy()
+    for i in range(len(pick)):
+        u = layout.unpack_stream(got_codes[i, 0], p, cap, T)
+        merge_counts(counts, classify(f[i][0], u, th, S[0], p))
+    ref, _ = attn.decode_cache(q[pick], f, V[pick], [(lv, th)], S, signs, None, p)
+    err = float(np.max(np.abs(out[pick_t].cpu().numpy() - ref)))
+    print(f"T {T}, splits {n_splits}: {counts}, max-abs {err:.2e}", flush=True)
+    assert_code_parity(counts)
+    assert err <= OUT_TOL and math.isfinite(err)
